@@ -1,0 +1,330 @@
+"""Plain, slow, obviously-correct CPU oracle for the MoGA forward hot path.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): the product path never
+imports this module.
+
+Source of every definition: the page "MoGA: Mixture-of-Groups Attention for
+End-to-End Long Video Generation" (architecture explainer of arXiv 2510.18692),
+sections "Vanilla Self-Attention and Its Computational Barrier in Video DiTs"
+(Eq. 1), "MoGA Router: Learned Per-Token Group Assignment" (routing scores,
+softmax gating Eq. 3, hard argmax assignment), "Grouped Attention: Computing
+Self-Attention Within Assigned Groups" (MoGA output equation),
+"MoGA Pseudocode and Kernel Integration" (Algorithm 1, steps 1-4),
+"Group Balancing Loss: Preventing Router Collapse" (Eq. 6 with F_i and P_i) and
+"Spatial-Temporal Group Attention (STGA): Complementary Local Attention".
+
+Precision: every floating-point step is evaluated in float64 from the exact
+input values (callers pass float arrays that hold bf16 values).  The single
+exception is the router's argmax, which is taken on the float32 rounding of
+the exact float64 logits, because that is the precision the GPU kernel decides
+in; inputs are generated so that the top-1 margin is far above that rounding.
+
+Readings of points the pages leave open (each is listed in the design doc):
+  * softmax scale is 1/sqrt(D) with D the per-head dimension;
+  * group ids are 0-based; argmax ties go to the lowest index;
+  * inside a group, tokens keep their original order (stable permutation);
+  * one routing decision per token, shared by every head;
+  * empty groups are allowed and produce no rows;
+  * the MoGA gate multiplies the attention output once, at unpermute time;
+  * STGA groups are fixed (t // win_t, y // tile_h, x // tile_w) windows over
+    frame-major tokens n = (t * Hs + y) * Ws + x, with no gate.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "router_logits",
+    "route",
+    "permute",
+    "gather_rows",
+    "group_attention",
+    "group_attention_rows",
+    "unpermute",
+    "stga_group_ids",
+    "stga_attention",
+    "stga_attention_rows",
+    "moga_forward",
+    "moga_output_rows",
+    "balance_stats",
+]
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Step 1: router ("MoGA Router" section; Algorithm 1 step 1)
+# ---------------------------------------------------------------------------
+
+def router_logits(X, Wr, bias=None) -> np.ndarray:
+    """Routing scores r = x W_r (+ optional bias), one row per token.
+
+    "MoGA Router" section, routing-score equation: a single linear map from the
+    hidden dimension to M scores.  ``Wr`` is stored as [M, d_model] (one
+    prototype per row), so r[n, i] = sum_k X[n, k] * Wr[i, k].
+    Evaluated in float64; products of bf16 values are exact there.
+    """
+    r = _f64(X) @ _f64(Wr).T
+    if bias is not None:
+        r = r + _f64(bias)[None, :]
+    return r
+
+
+def route(X, Wr, bias=None):
+    """Hard group assignment and gate for every token.
+
+    "MoGA Router" section: p(i|x) = softmax(r)_i (Eq. 3) and
+    g(x) = argmax_i p(i|x).  Because softmax is strictly increasing in each
+    score, the argmax of p is the argmax of r.  The gate used by the MoGA
+    output equation ("Grouped Attention" section) is p(g(x)|x)
+    = 1 / sum_j exp(r_j - r_g).
+
+    Returns (group_id int32[N], gate float32[N], logits float64[N, M]).
+    """
+    r64 = router_logits(X, Wr, bias)
+    # decision in float32, ties -> lowest index (numpy argmax convention)
+    g = np.argmax(r64.astype(np.float32), axis=1).astype(np.int32)
+    r_top = r64[np.arange(r64.shape[0]), g]
+    denom = np.exp(r64 - r_top[:, None]).sum(axis=1)
+    gate = (1.0 / denom).astype(np.float32)
+    return g, gate, r64
+
+
+# ---------------------------------------------------------------------------
+# Step 2: permutation by group ("MoGA Pseudocode", Algorithm 1 step 2)
+# ---------------------------------------------------------------------------
+
+def permute(group_id, M: int):
+    """Order tokens so group 0 comes first, then group 1, and so on.
+
+    Algorithm 1 step 2: the permuted sequence holds every token of group 0,
+    then every token of group 1, ...; cu_seqlens marks the group boundaries,
+    max_seqlen is the largest group and the permute index maps permuted
+    positions back to original tokens.  Within a group the original token
+    order is kept (a stable sort; the pages do not fix this order).
+
+    Returns (perm int32[N] with perm[j] = original token at permuted row j,
+             cu_seqlens int32[M+1], max_seqlen int).
+    """
+    g = np.asarray(group_id).astype(np.int64)
+    if g.size and (g.min() < 0 or g.max() >= M):
+        raise ValueError("group id out of range")
+    counts = np.bincount(g, minlength=M)
+    cu = np.zeros(M + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(counts)
+    perm = np.argsort(g, kind="stable").astype(np.int32)
+    max_seqlen = int(counts.max()) if M > 0 else 0
+    return perm, cu.astype(np.int32), max_seqlen
+
+
+def gather_rows(T, perm) -> np.ndarray:
+    """Permuted copy T_hat[j] = T[perm[j]] (Algorithm 1 step 2 applied to Q, K, V)."""
+    return np.asarray(T)[np.asarray(perm)]
+
+
+# ---------------------------------------------------------------------------
+# Step 3: self-attention inside every group (Eq. 1 per group; Algorithm 1 step 3)
+# ---------------------------------------------------------------------------
+
+def _softmax_rows_times_v(S, V):
+    """softmax over the last axis of S (float64), then times V (Eq. 1)."""
+    S = S - S.max(axis=-1, keepdims=True)
+    P = np.exp(S)
+    P /= P.sum(axis=-1, keepdims=True)
+    return P @ V
+
+
+def _group_of_rows(cu_seqlens, rows):
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    # group i holds permuted rows cu[i] .. cu[i+1]-1; empty groups never match
+    return np.searchsorted(cu, np.asarray(rows, dtype=np.int64), side="right") - 1
+
+
+def group_attention_rows(Qp, Kp, Vp, cu_seqlens, scale, rows, heads=None):
+    """Attention output of selected permuted rows, every head unless ``heads``.
+
+    For permuted row j in group i and head h (Eq. 1 restricted to the group,
+    Algorithm 1 step 3): O[j, h] = softmax(q_jh . K_ih^T * scale) V_ih, where
+    K_ih, V_ih are rows cu[i] .. cu[i+1]-1 of head h.  Non-causal; the token
+    attends to itself.  Returns float64 [len(rows), H_sel, D].
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    Hn = Qp.shape[1]
+    heads = np.arange(Hn) if heads is None else np.asarray(heads, dtype=np.int64)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    out = np.zeros((rows.size, heads.size, Qp.shape[2]), dtype=np.float64)
+    grp = _group_of_rows(cu, rows)
+    for i in np.unique(grp):
+        sel = np.nonzero(grp == i)[0]
+        lo, hi = cu[i], cu[i + 1]
+        for a, h in enumerate(heads):
+            q = _f64(Qp[rows[sel], h, :])
+            k = _f64(Kp[lo:hi, h, :])
+            v = _f64(Vp[lo:hi, h, :])
+            out[sel, a, :] = _softmax_rows_times_v((q @ k.T) * scale, v)
+    return out
+
+
+def group_attention(Qp, Kp, Vp, cu_seqlens, scale, row_block: int = 2048):
+    """Attention of every permuted row within its group (float64 [N, H, D]).
+
+    Rows are evaluated ``row_block`` at a time only to bound memory; each row's
+    softmax is independent of the others, so this is the same definition.
+    """
+    N = Qp.shape[0]
+    out = np.zeros((N, Qp.shape[1], Qp.shape[2]), dtype=np.float64)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    for i in range(cu.size - 1):
+        lo, hi = int(cu[i]), int(cu[i + 1])
+        for s in range(lo, hi, row_block):
+            r = np.arange(s, min(hi, s + row_block))
+            out[r] = group_attention_rows(Qp, Kp, Vp, cu, scale, r)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Step 4: gate and unpermute ("Grouped Attention" output equation; Algorithm 1 step 4)
+# ---------------------------------------------------------------------------
+
+def unpermute(Op, perm, gate, beta: float = 0.0, O_prev=None):
+    """O[perm[j]] = beta * O_prev[perm[j]] + gate[perm[j]] * Op[j].
+
+    The MoGA output equation multiplies the in-group attention of token x by
+    p(g(x)|x); Algorithm 1 step 4 returns rows to their original positions.
+    ``beta`` = 0 overwrites, 1 adds onto ``O_prev`` (used to sum with STGA).
+    """
+    perm = np.asarray(perm, dtype=np.int64)
+    g64 = _f64(gate)
+    out = np.zeros(Op.shape, dtype=np.float64)
+    out[perm] = g64[perm][:, None, None] * _f64(Op)
+    if beta != 0.0:
+        out += beta * _f64(O_prev)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# STGA branch ("Spatial-Temporal Group Attention (STGA)" section)
+# ---------------------------------------------------------------------------
+
+def stga_group_ids(T, Hs, Ws, win_t, tile_h, tile_w) -> np.ndarray:
+    """Static group of every frame-major token n = (t*Hs + y)*Ws + x.
+
+    STGA section: the latent grid is split into fixed spatial windows and
+    frames are grouped along time.  Here the spatial windows are tile_h x
+    tile_w and the temporal groups are consecutive runs of win_t frames.
+    Group id = ((t // win_t) * (Hs // tile_h) + y // tile_h) * (Ws // tile_w)
+               + x // tile_w.
+    """
+    if T % win_t or Hs % tile_h or Ws % tile_w:
+        raise ValueError("STGA windows must tile the latent grid")
+    ids = np.empty((T, Hs, Ws), dtype=np.int64)
+    for t in range(T):
+        for y in range(Hs):
+            for x in range(Ws):
+                ids[t, y, x] = ((t // win_t) * (Hs // tile_h) + y // tile_h) * (Ws // tile_w) + x // tile_w
+    return ids.reshape(-1)
+
+
+def stga_attention_rows(Q, K, V, ids, scale, rows):
+    """STGA output of selected original rows: softmax attention over the
+    tokens that share the row's static group (float64 [len(rows), H, D])."""
+    rows = np.asarray(rows, dtype=np.int64)
+    ids = np.asarray(ids)
+    out = np.zeros((rows.size, Q.shape[1], Q.shape[2]), dtype=np.float64)
+    for gid in np.unique(ids[rows]):
+        sel = np.nonzero(ids[rows] == gid)[0]
+        members = np.nonzero(ids == gid)[0]
+        for h in range(Q.shape[1]):
+            q = _f64(Q[rows[sel], h, :])
+            k = _f64(K[members, h, :])
+            v = _f64(V[members, h, :])
+            out[sel, h, :] = _softmax_rows_times_v((q @ k.T) * scale, v)
+    return out
+
+
+def stga_attention(Q, K, V, T, Hs, Ws, win_t, tile_h, tile_w, scale,
+                   alpha: float = 1.0, beta: float = 0.0, O_prev=None):
+    """O = beta * O_prev + alpha * STGA(Q, K, V) over every token (float64)."""
+    ids = stga_group_ids(T, Hs, Ws, win_t, tile_h, tile_w)
+    if ids.size != Q.shape[0]:
+        raise ValueError("T*Hs*Ws must equal N")
+    out = alpha * stga_attention_rows(Q, K, V, ids, scale, np.arange(Q.shape[0]))
+    if beta != 0.0:
+        out += beta * _f64(O_prev)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Whole forward path (Algorithm 1 steps 1-4, plus the optional STGA sum)
+# ---------------------------------------------------------------------------
+
+def moga_forward(X, Wr, Q, K, V, M: int, scale=None, bias=None, stga=None):
+    """Full MoGA forward on original token order.
+
+    ``stga`` is None or a dict with T, Hs, Ws, win_t, tile_h, tile_w and the
+    weights alpha (STGA) / beta (MoGA); the result is then
+    beta * MoGA + alpha * STGA.  Returns a dict with every intermediate.
+    """
+    D = Q.shape[2]
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    g, gate, r = route(X, Wr, bias)
+    perm, cu, max_seqlen = permute(g, M)
+    Qp, Kp, Vp = gather_rows(Q, perm), gather_rows(K, perm), gather_rows(V, perm)
+    Op = group_attention(Qp, Kp, Vp, cu, scale)
+    O = unpermute(Op, perm, gate)
+    if stga is not None:
+        S = stga_attention(Q, K, V, stga["T"], stga["Hs"], stga["Ws"], stga["win_t"],
+                           stga["tile_h"], stga["tile_w"], scale)
+        O = stga.get("beta", 1.0) * O + stga.get("alpha", 1.0) * S
+    return {"group_id": g, "gate": gate, "logits": r, "perm": perm, "cu_seqlens": cu,
+            "max_seqlen": max_seqlen, "Op": Op, "O": O}
+
+
+def moga_output_rows(X, Wr, Q, K, V, M: int, rows, scale=None, bias=None, routed=None):
+    """MoGA output at selected ORIGINAL token rows, without the full pass.
+
+    For token n in group g: O[n] = gate_n * SA(q_n, K_g, V_g) (MoGA output
+    equation).  ``routed`` may pass a precomputed (group_id, gate) pair.
+    Returns float64 [len(rows), H, D].
+    """
+    D = Q.shape[2]
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    if routed is None:
+        g, gate, _ = route(X, Wr, bias)
+    else:
+        g, gate = routed
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.zeros((rows.size, Q.shape[1], D), dtype=np.float64)
+    for grp in np.unique(g[rows]):
+        sel = np.nonzero(g[rows] == grp)[0]
+        members = np.nonzero(g == grp)[0]  # original order; attention is order-free
+        for h in range(Q.shape[1]):
+            q = _f64(Q[rows[sel], h, :])
+            k = _f64(K[members, h, :])
+            v = _f64(V[members, h, :])
+            out[sel, h, :] = _softmax_rows_times_v((q @ k.T) * scale, v)
+    out *= _f64(gate)[rows][:, None, None]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Group-balancing statistics ("Group Balancing Loss" section, Eq. 6)
+# ---------------------------------------------------------------------------
+
+def balance_stats(group_id, gate, M: int, alpha: float = 0.1):
+    """F_i, P_i and L_gb = alpha * M * sum_i F_i P_i.
+
+    F_i = (1/N) * #{x : g(x) = i};  P_i = (1/N) * sum over tokens with
+    g(x) = i of p(g(x)|x), taking the equation's 1/N literally (the prose
+    beside it speaks of a per-group average; that reading is not used).
+    """
+    g = np.asarray(group_id, dtype=np.int64)
+    N = g.size
+    F = np.bincount(g, minlength=M).astype(np.float64) / N
+    P = np.bincount(g, weights=_f64(gate), minlength=M) / N
+    return F, P, alpha * M * float(np.sum(F * P))

@@ -1,0 +1,54 @@
+"""Parity bars shared by the CPU and GPU tests.
+
+bf16 outputs (read back as float) are compared element by element with the
+oracle's float64 values: max-abs <= 2e-2 and mean-abs <= 2e-3 (the stated
+bar), plus relative Frobenius error <= 1e-2 so that small-magnitude outputs
+cannot pass on the absolute bars alone.
+"""
+
+import numpy as np
+
+MAX_ABS = 2e-2
+MEAN_ABS = 2e-3
+REL_FRO = 1e-2
+GATE_RTOL = 1e-4  # float32 gate; derivation in DESIGN.md ("Tolerances")
+
+
+def output_errors(got, want):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    diff = np.abs(got - want)
+    denom = max(float(np.linalg.norm(want)), 1e-300)
+    return {
+        "max_abs": float(diff.max()) if diff.size else 0.0,
+        "mean_abs": float(diff.mean()) if diff.size else 0.0,
+        "rel_fro": float(np.linalg.norm(got - want) / denom) if diff.size else 0.0,
+        "scale": float(np.abs(want).mean()) if diff.size else 0.0,
+        "finite": bool(np.isfinite(got).all()),
+    }
+
+
+def output_ok(e):
+    return e["finite"] and e["max_abs"] <= MAX_ABS and e["mean_abs"] <= MEAN_ABS and e["rel_fro"] <= REL_FRO
+
+
+def assert_output_close(got, want, what="O"):
+    e = output_errors(got, want)
+    assert output_ok(e), f"{what}: {e} exceeds max_abs {MAX_ABS} / mean_abs {MEAN_ABS} / rel_fro {REL_FRO}"
+    return e
+
+
+def assert_gate_close(got, want):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    rel = np.abs(got - want) / np.abs(want)
+    assert rel.max() <= GATE_RTOL, f"gate rel err {rel.max():.3g} > {GATE_RTOL}"
+    return float(rel.max())
+
+
+def bf16_round(a):
+    """Round-to-nearest-even float64 -> bf16 -> float64 (for negative controls)."""
+    f = np.asarray(a, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
