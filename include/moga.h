@@ -1,0 +1,157 @@
+/*
+ * moga.h -- C ABI of the MoGA (Mixture-of-Groups Attention) forward hot path
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Source of the operations: the page "MoGA: Mixture-of-Groups Attention for
+ * End-to-End Long Video Generation" (architecture explainer of arXiv
+ * 2510.18692).  Section names below refer to that page.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or synchronises; every launch goes to `stream`
+ *    (a hipStream_t passed as void*; NULL = the null stream) and returns
+ *    without waiting.  Scratch memory ("workspace") is caller-allocated, sized
+ *    by moga_workspace_bytes().
+ *  - bf16 tensors are passed as void* holding IEEE bfloat16 values.  Every
+ *    bf16 result is rounded to nearest-even from float32.
+ *  - Token tensors Q, K, V, Q_hat, K_hat, V_hat, O_hat and O are contiguous
+ *    [N, H, D] (token-major, then head, then channel).  X is [N, d_model];
+ *    W_r is [M, d_model] (one prototype per row).
+ *  - Group ids are 0-based int32.  cu_seqlens is int32 [M+1] with
+ *    cu_seqlens[0] = 0, cu_seqlens[M] = N; an empty group repeats an entry.
+ *  - Supported ranges: 1 <= M <= 64; D in {64, 128}; 1 <= H; H*D <= 8192;
+ *    1 <= N < 2^31; d_model a positive multiple of 32.
+ *  - Return value: MOGA_OK (0) or a negative moga_status.  Argument errors are
+ *    found on the host before anything is launched, and then no output buffer
+ *    is touched.  Faults inside kernels surface at the caller's next
+ *    synchronisation.  Inputs must be finite; group ids outside [0, M) are a
+ *    precondition violation and are not checked on the device.
+ *  - Calls on different streams may run concurrently; each call only reads
+ *    its inputs and writes its outputs and workspace.
+ */
+#ifndef MOGA_H_
+#define MOGA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moga_status {
+  MOGA_OK = 0,
+  MOGA_ERR_NULL = -1,        /* a required pointer is NULL */
+  MOGA_ERR_SHAPE = -2,       /* a size is out of range or sizes disagree */
+  MOGA_ERR_UNSUPPORTED = -3, /* a valid but unsupported configuration (e.g. D = 96) */
+  MOGA_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than moga_workspace_bytes() */
+  MOGA_ERR_HIP = -5          /* the HIP runtime refused a launch */
+} moga_status;
+
+typedef enum moga_op {
+  MOGA_OP_ROUTE = 0,
+  MOGA_OP_PERMUTE = 1,
+  MOGA_OP_GROUP_ATTENTION = 2,
+  MOGA_OP_UNPERMUTE = 3,
+  MOGA_OP_STGA_ATTENTION = 4
+} moga_op;
+
+/*
+ * moga_route -- router scores, hard assignment and gate for every token.
+ *   Section "MoGA Router": r = x W_r (+ optional bias), p(i|x) = softmax(r)_i
+ *   (Eq. 3), g(x) = argmax_i p(i|x); Algorithm 1 step 1.  The gate is
+ *   p(g(x)|x) = 1 / sum_j exp(r_j - r_g), used by the MoGA output equation
+ *   ("Grouped Attention").  Scores are accumulated in float32; the argmax is
+ *   taken on the float32 scores, ties going to the lowest group index.
+ *   X        bf16 [N, d_model]
+ *   Wr       bf16 [M, d_model]
+ *   bias     float [M] or NULL (no bias)
+ *   group_id int32 [N]  (output)
+ *   gate     float [N]  (output)
+ *   Needs no workspace.
+ */
+int moga_route(const void* X, const void* Wr, const float* bias,
+               int64_t N, int32_t d_model, int32_t M,
+               int32_t* group_id, float* gate, void* stream);
+
+/*
+ * moga_permute -- make every group contiguous (Algorithm 1 step 2).
+ *   Groups are laid out in increasing id; inside a group tokens keep their
+ *   original order (stable counting sort).
+ *   group_id   int32 [N] (input, values in [0, M))
+ *   Q, K, V    bf16 [N, H, D] (inputs)
+ *   Qp, Kp, Vp bf16 [N, H, D] (outputs): Qp[j] = Q[perm[j]], likewise K, V
+ *   perm       int32 [N]   (output): original token of permuted row j
+ *   cu_seqlens int32 [M+1] (output): group boundaries in permuted order
+ *   max_seqlen int32 [1]   (output, device scalar): largest group size
+ *   ws         workspace of at least moga_workspace_bytes(MOGA_OP_PERMUTE, N, M, H, D) bytes
+ *   Q, K, V, Qp, Kp, Vp may ALL be NULL: then only perm, cu_seqlens and
+ *   max_seqlen are produced (H and D are then ignored).
+ */
+int moga_permute(const int32_t* group_id, const void* Q, const void* K, const void* V,
+                 int64_t N, int32_t H, int32_t D, int32_t M,
+                 void* Qp, void* Kp, void* Vp, int32_t* perm, int32_t* cu_seqlens,
+                 int32_t* max_seqlen, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moga_group_attention -- exact softmax attention inside every group
+ *   (Eq. 1 restricted to a group; Algorithm 1 step 3), non-causal, each token
+ *   attending to itself and every other token of its group, for every head.
+ *   Qp, Kp, Vp  bf16 [N, H, D], rows grouped as described by cu_seqlens
+ *   cu_seqlens  int32 [M+1] (device)
+ *   softmax_scale  > 0, or <= 0 for 1/sqrt(D)
+ *   Op          bf16 [N, H, D] (output, permuted order, no gate)
+ *   ws          workspace of at least moga_workspace_bytes(MOGA_OP_GROUP_ATTENTION, N, M, H, D)
+ *   bf16 MFMA products, float32 accumulation and online softmax.
+ */
+int moga_group_attention(const void* Qp, const void* Kp, const void* Vp,
+                         const int32_t* cu_seqlens, int64_t N, int32_t H, int32_t D,
+                         int32_t M, float softmax_scale, void* Op,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moga_unpermute -- gate and return rows to original order
+ *   (MoGA output equation in "Grouped Attention"; Algorithm 1 step 4):
+ *   O[perm[j]] = beta * O[perm[j]] + gate[perm[j]] * Op[j]  (float32 math).
+ *   beta = 0 overwrites O (its old contents are not read); beta != 0
+ *   accumulates, e.g. onto an STGA result.
+ *   Op bf16 [N, H, D]; perm int32 [N]; gate float [N]; O bf16 [N, H, D] (in/out).
+ *   Needs no workspace.
+ */
+int moga_unpermute(const void* Op, const int32_t* perm, const float* gate,
+                   int64_t N, int32_t H, int32_t D, float beta, void* O, void* stream);
+
+/*
+ * moga_stga_attention -- static local window attention (section "Spatial-
+ *   Temporal Group Attention (STGA)"): tokens are frame-major,
+ *   n = (t * Hs + y) * Ws + x with N = T * Hs * Ws, and token n belongs to the
+ *   static group (t / win_t, y / tile_h, x / tile_w).  Softmax attention runs
+ *   inside each static group, on the original token order, without a gate:
+ *   O[n] = beta * O[n] + alpha * STGA(n)   (beta = 0: O is not read).
+ *   Q, K, V bf16 [N, H, D]; O bf16 [N, H, D] (in/out).
+ *   win_t, tile_h, tile_w must divide T, Hs, Ws; the group size
+ *   win_t * tile_h * tile_w must be at most 2^20.  Needs no workspace.
+ */
+int moga_stga_attention(const void* Q, const void* K, const void* V,
+                        int32_t T, int32_t Hs, int32_t Ws, int32_t win_t, int32_t tile_h,
+                        int32_t tile_w, int32_t H, int32_t D, float softmax_scale,
+                        float alpha, float beta, void* O, void* stream);
+
+/*
+ * moga_workspace_bytes -- bytes of workspace `op` needs for these sizes
+ *   (0 when the op needs none, or when the sizes are invalid).  Host-only.
+ */
+size_t moga_workspace_bytes(int32_t op, int64_t N, int32_t M, int32_t H, int32_t D);
+
+/* moga_strerror -- static description of a moga_status.  Host-only. */
+const char* moga_strerror(int32_t status);
+
+/* moga_version -- library version as major * 10000 + minor * 100 + patch. */
+int32_t moga_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOGA_H_ */

@@ -1,0 +1,181 @@
+"""Python entry points with the names of the C ABI (include/moga.h).
+
+Each function checks tensor placement, dtype and shape, allocates missing
+outputs with torch (device memory is all torch provides here) and calls the
+library on the current HIP stream.  No arithmetic of the method happens in
+Python.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import (MOGA_OP_GROUP_ATTENTION, MOGA_OP_PERMUTE, check, ptr, stream_handle)
+
+BF16 = torch.bfloat16
+
+
+def _need(t, name, dtype=None, ndim=None, shape=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def moga_workspace_bytes(op: int, N: int, M: int, H: int = 1, D: int = 64) -> int:
+    return _lib.workspace_bytes(op, N, M, H, D)
+
+
+def _workspace(op, N, M, H, D, ws, device):
+    need = moga_workspace_bytes(op, N, M, H, D)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    _need(ws, "ws")
+    return ws, ws.numel() * ws.element_size()
+
+
+def moga_route(X, Wr, bias=None, group_id=None, gate=None):
+    """group_id int32 [N], gate float32 [N] from X [N, d] and W_r [M, d] (bf16)."""
+    _need(X, "X", BF16, 2)
+    M, d = Wr.shape
+    _need(Wr, "Wr", BF16, 2, (M, X.shape[1]))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, 1, (M,))
+    N = X.shape[0]
+    group_id = torch.empty(N, dtype=torch.int32, device=X.device) if group_id is None else group_id
+    gate = torch.empty(N, dtype=torch.float32, device=X.device) if gate is None else gate
+    _need(group_id, "group_id", torch.int32, 1, (N,))
+    _need(gate, "gate", torch.float32, 1, (N,))
+    check(_lib.LIB.moga_route(ptr(X), ptr(Wr), ptr(bias), N, d, M, ptr(group_id), ptr(gate), stream_handle()),
+          "moga_route")
+    return group_id, gate
+
+
+def moga_permute(group_id, M, Q=None, K=None, V=None, Qp=None, Kp=None, Vp=None, perm=None, cu_seqlens=None,
+                 max_seqlen=None, ws=None):
+    """Stable group permutation; gathers Q/K/V when given.  Returns a dict."""
+    _need(group_id, "group_id", torch.int32, 1)
+    N = group_id.shape[0]
+    dev = group_id.device
+    rows = Q is not None
+    H = D = 1
+    if rows:
+        _need(Q, "Q", BF16, 3)
+        H, D = Q.shape[1], Q.shape[2]
+        for name, t in (("K", K), ("V", V)):
+            _need(t, name, BF16, 3, Q.shape)
+        if Q.shape[0] != N:
+            raise ValueError("Q rows must match group_id")
+        Qp = torch.empty_like(Q) if Qp is None else Qp
+        Kp = torch.empty_like(K) if Kp is None else Kp
+        Vp = torch.empty_like(V) if Vp is None else Vp
+        for name, t in (("Qp", Qp), ("Kp", Kp), ("Vp", Vp)):
+            _need(t, name, BF16, 3, Q.shape)
+    perm = torch.empty(N, dtype=torch.int32, device=dev) if perm is None else perm
+    cu_seqlens = torch.empty(M + 1, dtype=torch.int32, device=dev) if cu_seqlens is None else cu_seqlens
+    max_seqlen = torch.empty(1, dtype=torch.int32, device=dev) if max_seqlen is None else max_seqlen
+    _need(perm, "perm", torch.int32, 1, (N,))
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1, (M + 1,))
+    _need(max_seqlen, "max_seqlen", torch.int32, 1, (1,))
+    ws, nbytes = _workspace(MOGA_OP_PERMUTE, N, M, H, D, ws, dev)
+    check(_lib.LIB.moga_permute(ptr(group_id), ptr(Q), ptr(K), ptr(V), N, H, D, M, ptr(Qp), ptr(Kp), ptr(Vp),
+                                ptr(perm), ptr(cu_seqlens), ptr(max_seqlen), ptr(ws), nbytes, stream_handle()),
+          "moga_permute")
+    return {"Qp": Qp, "Kp": Kp, "Vp": Vp, "perm": perm, "cu_seqlens": cu_seqlens, "max_seqlen": max_seqlen}
+
+
+def moga_group_attention(Qp, Kp, Vp, cu_seqlens, softmax_scale=0.0, Op=None, ws=None):
+    """Attention inside each group of the permuted Q/K/V (bf16 [N, H, D])."""
+    _need(Qp, "Qp", BF16, 3)
+    N, H, D = Qp.shape
+    _need(Kp, "Kp", BF16, 3, Qp.shape)
+    _need(Vp, "Vp", BF16, 3, Qp.shape)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    M = cu_seqlens.shape[0] - 1
+    Op = torch.empty_like(Qp) if Op is None else Op
+    _need(Op, "Op", BF16, 3, Qp.shape)
+    ws, nbytes = _workspace(MOGA_OP_GROUP_ATTENTION, N, M, H, D, ws, Qp.device)
+    check(_lib.LIB.moga_group_attention(ptr(Qp), ptr(Kp), ptr(Vp), ptr(cu_seqlens), N, H, D, M,
+                                        float(softmax_scale), ptr(Op), ptr(ws), nbytes, stream_handle()),
+          "moga_group_attention")
+    return Op
+
+
+def moga_unpermute(Op, perm, gate, beta=0.0, O=None):
+    """O[perm[j]] = beta * O[perm[j]] + gate[perm[j]] * Op[j]."""
+    _need(Op, "Op", BF16, 3)
+    N, H, D = Op.shape
+    _need(perm, "perm", torch.int32, 1, (N,))
+    _need(gate, "gate", torch.float32, 1, (N,))
+    if O is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs an existing O")
+        O = torch.empty_like(Op)
+    _need(O, "O", BF16, 3, Op.shape)
+    check(_lib.LIB.moga_unpermute(ptr(Op), ptr(perm), ptr(gate), N, H, D, float(beta), ptr(O), stream_handle()),
+          "moga_unpermute")
+    return O
+
+
+def moga_stga_attention(Q, K, V, T, Hs, Ws, win_t, tile_h, tile_w, softmax_scale=0.0, alpha=1.0, beta=0.0,
+                        O=None):
+    """Static window attention over frame-major tokens; O = beta*O + alpha*STGA."""
+    _need(Q, "Q", BF16, 3)
+    N, H, D = Q.shape
+    _need(K, "K", BF16, 3, Q.shape)
+    _need(V, "V", BF16, 3, Q.shape)
+    if O is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs an existing O")
+        O = torch.empty_like(Q)
+    _need(O, "O", BF16, 3, Q.shape)
+    if T * Hs * Ws != N:
+        raise ValueError("T*Hs*Ws must equal N")
+    check(_lib.LIB.moga_stga_attention(ptr(Q), ptr(K), ptr(V), T, Hs, Ws, win_t, tile_h, tile_w, H, D,
+                                       float(softmax_scale), float(alpha), float(beta), ptr(O), stream_handle()),
+          "moga_stga_attention")
+    return O
+
+
+class MogaForward:
+    """Preallocated buffers for one MoGA layer pass (route, permute, group
+    attention, unpermute and, when ``stga`` geometry is given, the STGA sum).
+    ``__call__`` launches the five library calls back to back on the current
+    stream and allocates nothing."""
+
+    def __init__(self, N, d_model, H, D, M, device, stga=None):
+        self.N, self.d_model, self.H, self.D, self.M, self.stga = N, d_model, H, D, M, stga
+        e = lambda *s, dt=BF16: torch.empty(*s, dtype=dt, device=device)  # noqa: E731
+        self.group_id = e(N, dt=torch.int32)
+        self.gate = e(N, dt=torch.float32)
+        self.Qp, self.Kp, self.Vp, self.Op, self.O = (e(N, H, D) for _ in range(5))
+        self.perm = e(N, dt=torch.int32)
+        self.cu_seqlens = e(M + 1, dt=torch.int32)
+        self.max_seqlen = e(1, dt=torch.int32)
+        self.ws_perm = e(max(moga_workspace_bytes(MOGA_OP_PERMUTE, N, M, H, D), 1), dt=torch.uint8)
+        self.ws_attn = e(max(moga_workspace_bytes(MOGA_OP_GROUP_ATTENTION, N, M, H, D), 1), dt=torch.uint8)
+
+    def __call__(self, X, Wr, Q, K, V, bias=None, softmax_scale=0.0, stga_weight=1.0, moga_weight=1.0):
+        """O = moga_weight * MoGA + stga_weight * STGA (the STGA term only with geometry)."""
+        moga_route(X, Wr, bias, self.group_id, self.gate)
+        moga_permute(self.group_id, self.M, Q, K, V, self.Qp, self.Kp, self.Vp, self.perm, self.cu_seqlens,
+                     self.max_seqlen, self.ws_perm)
+        moga_group_attention(self.Qp, self.Kp, self.Vp, self.cu_seqlens, softmax_scale, self.Op, self.ws_attn)
+        moga_unpermute(self.Op, self.perm, self.gate, 0.0, self.O)
+        if self.stga is not None:
+            g = self.stga
+            moga_stga_attention(Q, K, V, g["T"], g["Hs"], g["Ws"], g["win_t"], g["tile_h"], g["tile_w"],
+                                softmax_scale, stga_weight, moga_weight, self.O)
+        elif moga_weight != 1.0:
+            raise ValueError("moga_weight applies only together with an STGA branch")
+        return self.O

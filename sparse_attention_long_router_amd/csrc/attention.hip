@@ -1,0 +1,345 @@
+// Group attention for gfx950: exact softmax attention inside every group, for
+// the learned MoGA groups (variable length, permuted rows) and for the static
+// STGA windows (fixed size, rows gathered by an index map).
+// Page "MoGA: Mixture-of-Groups Attention for End-to-End Long Video
+// Generation": Eq. 1 (softmax(q K^T / sqrt(d)) V) restricted to a group, as in
+// the MoGA output equation ("Grouped Attention") and Algorithm 1 step 3; the
+// static windows are those of the "Spatial-Temporal Group Attention (STGA)"
+// section.  The online (running max / running sum) softmax is the one of the
+// FlashAttention papers the pages cite; the tiling here is our own for CDNA4.
+//
+// Work item = (group, head, tile of 128 queries); a workgroup of 4 waves owns
+// one item, each wave 32 queries.  Per 64-key tile:
+//   K and V rows are staged in LDS (16-byte XOR-swizzled chunks, conflict-free
+//   writes and reads);
+//   S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = the
+//   wave's Q fragment held in registers) -- the C layout gives every lane one
+//   query and 16 keys, so the softmax statistics stay in-lane (the two wave
+//   halves share a query and exchange one value);
+//   online softmax in float32 with exp2 and the scale folded into one FMA;
+//   O^T += V^T P^T with the same MFMA: B = P^T comes straight from the S^T
+//   registers (the k-slot order of an MFMA is free as long as both operands
+//   agree), A = V^T comes from row-major V in LDS through ds_read_b64_tr_b16.
+// Items are handed out largest group first (longest-processing-time order) and
+// dealt to the 8 XCDs in runs of consecutive query tiles of one (group, head),
+// so tiles that stream the same K/V run side by side under one L2.
+#include "moga_internal.h"
+
+namespace moga {
+namespace {
+
+constexpr int kAttnWaves = 4;
+constexpr int kQueriesPerWave = 32;
+constexpr int kBM = kAttnWaves * kQueriesPerWave;  // queries per workgroup
+constexpr int kBN = 64;                             // keys per LDS tile
+constexpr int kXcdRun = 8;                          // consecutive items per XCD
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+struct Work {
+  int len;      // group size
+  int q0;       // first query (group-local) of this item
+  int head;
+  int64_t row0; // MoGA: first permuted row of the group
+  int t0, y0, x0;  // STGA: window origin
+};
+
+// Learned groups: rows of group g are cu[g] .. cu[g+1]-1 of the permuted tensors.
+struct MogaRows {
+  const int32_t* cu;
+  const AttnSchedule* sched;
+  int M, H;
+  __device__ __forceinline__ bool decode(int item, Work& w) const {
+    const int total = sched->prefix[M];
+    if (item >= total) return false;
+    int i = 0;
+    while (i + 1 < M && sched->prefix[i + 1] <= item) ++i;
+    const int g = sched->order[i];
+    const int local = item - sched->prefix[i];
+    const int lo = cu[g];
+    const int len = cu[g + 1] - lo;
+    const int nt = (len + kBM - 1) / kBM;
+    w.len = len;
+    w.head = local / nt;
+    w.q0 = (local - w.head * nt) * kBM;
+    w.row0 = lo;
+    return true;
+  }
+  __device__ __forceinline__ int64_t row(const Work& w, int i) const { return w.row0 + i; }
+};
+
+// Static windows over frame-major tokens n = (t*Hs + y)*Ws + x.
+struct StgaRows {
+  int Hs, Ws, win_t, tile_h, tile_w, nty, ntx, tiles_per_group, H, items;
+  __device__ __forceinline__ bool decode(int item, Work& w) const {
+    if (item >= items) return false;
+    const int per_group = H * tiles_per_group;
+    const int grp = item / per_group;
+    const int rem = item - grp * per_group;
+    w.head = rem / tiles_per_group;
+    w.q0 = (rem - w.head * tiles_per_group) * kBM;
+    w.len = win_t * tile_h * tile_w;
+    const int tw = grp / (nty * ntx);
+    const int r2 = grp - tw * (nty * ntx);
+    const int ty = r2 / ntx;
+    w.t0 = tw * win_t;
+    w.y0 = ty * tile_h;
+    w.x0 = (r2 - ty * ntx) * tile_w;
+    w.row0 = 0;
+    return true;
+  }
+  __device__ __forceinline__ int64_t row(const Work& w, int i) const {
+    const int area = tile_h * tile_w;
+    const int tt = i / area;
+    const int rem = i - tt * area;
+    const int yy = rem / tile_w;
+    const int xx = rem - yy * tile_w;
+    return ((int64_t)(w.t0 + tt) * Hs + (w.y0 + yy)) * Ws + (w.x0 + xx);
+  }
+};
+
+// 16-byte chunk swizzles of the K and V tiles in LDS (cpr = chunks per row).
+__device__ __forceinline__ int kswz(int r, int cpr) { return r & (cpr - 1); }
+__device__ __forceinline__ int vswz(int r, int cpr) { return ((r & 3) << 2) & (cpr - 1); }
+
+template <int D, class Rows, bool kStga>
+__global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    uint16_t* __restrict__ O, int64_t row_stride, float scale_log2, float alpha, float beta, Rows rows) {
+  constexpr int CPR = D / 8;       // 16-byte chunks per row
+  constexpr int KSTEPS = D / 16;   // MFMA k-steps over the head dimension
+  constexpr int DBLK = D / 32;     // 32-wide output blocks
+  constexpr int STAGE_ITERS = kBN * CPR / (kAttnWaves * kWave);
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[kBN * D];
+
+  Work w;
+  if (!rows.decode(xcd_remap(blockIdx.x, kXcdRun), w)) return;  // uniform per block
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hh = lane >> 5, c = lane & 31;
+  const int64_t hoff = (int64_t)w.head * D;
+
+  // ---- this lane's query and its Q fragment (B operand of S^T = K Q^T)
+  const int qi = w.q0 + wave * kQueriesPerWave + c;
+  const bool qvalid = qi < w.len;
+  const int64_t qrow = rows.row(w, qvalid ? qi : w.len - 1);
+  bf16x8 qf[KSTEPS];
+  {
+    const uint16_t* qp = Q + qrow * row_stride + hoff + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
+  }
+
+  f32x16 o[DBLK];
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db) o[db] = f32x16{};
+  float m_run = -INFINITY;  // running max of the scaled (log2-domain) scores
+  float l_run = 0.f;        // this lane's share of the running denominator
+
+  // tr-read roles (see the operand map in the header comment)
+  const int tr_r = (lane & 15) >> 2, tr_q = lane & 3, tr_g = (lane >> 4) & 1;
+
+  for (int k0 = 0; k0 < w.len; k0 += kBN) {
+    // ---- stage K, V rows k0 .. k0+63 (zero rows past the group end)
+#pragma unroll
+    for (int it = 0; it < STAGE_ITERS; ++it) {
+      const int idx = it * (kAttnWaves * kWave) + tid;
+      const int r = idx / CPR, ch = idx % CPR;
+      const int key = k0 + r;
+      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      if (key < w.len) {
+        const int64_t off = rows.row(w, key) * row_stride + hoff + ch * 8;
+        kv = *reinterpret_cast<const u32x4*>(K + off);
+        vv = *reinterpret_cast<const u32x4*>(V + off);
+      }
+      *reinterpret_cast<u32x4*>(Ks + r * D + (ch ^ kswz(r, CPR)) * 8) = kv;
+      *reinterpret_cast<u32x4*>(Vs + r * D + (ch ^ vswz(r, CPR)) * 8) = vv;
+    }
+    __syncthreads();
+
+    // ---- S^T = K Q^T: two 32-key blocks; reg r of block kb is key
+    //      kb*32 + 8*(r/4) + 4*hh + r%4 of this tile, query c
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      const int krow = kb * 32 + c;
+#pragma unroll
+      for (int st = 0; st < KSTEPS; ++st) {
+        const int ch = 2 * st + hh;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + krow * D + (ch ^ kswz(krow, CPR)) * 8);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[kb], 0, 0, 0);
+      }
+    }
+    if (k0 + kBN > w.len) {  // last, partial tile
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (key >= w.len) s[kb][r] = -INFINITY;
+        }
+    }
+
+    // ---- online softmax (log2 domain)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx * scale_log2);
+    const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale_log2, -m_new));
+        s[kb][r] = p;
+        rs += p;
+      }
+    l_run = l_run * corr + rs;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) o[db] *= corr;
+
+    // ---- O^T += V^T P^T, 16 keys per MFMA
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        bf16x8 pb;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pb[j] = (__bf16)s[kb][8 * t + j];
+        const int r1 = kb * 32 + 16 * t + 4 * hh + tr_r;
+        const int r2 = r1 + 8;
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) {
+          const int col = 32 * db + 16 * tr_g + 4 * tr_q;
+          const int ch = col >> 3, within = col & 7;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(Vs + r1 * D + ((ch ^ vswz(r1, CPR)) << 3) + within));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(Vs + r2 * D + ((ch ^ vswz(r2, CPR)) << 3) + within));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[db], 0, 0, 0);
+        }
+      }
+    __syncthreads();  // the next tile overwrites Ks / Vs
+  }
+
+  // ---- normalise and store: reg r of block db is channel 32*db + 8*(r/4) + 4*hh + r%4
+  const float inv = 1.0f / (l_run + __shfl_xor(l_run, 32));
+  if (qvalid) {
+    uint16_t* op = O + qrow * row_stride + hoff;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int d0 = 32 * db + 8 * b + 4 * hh;
+        float v0 = o[db][4 * b] * inv, v1 = o[db][4 * b + 1] * inv;
+        float v2 = o[db][4 * b + 2] * inv, v3 = o[db][4 * b + 3] * inv;
+        if constexpr (kStga) {
+          v0 *= alpha; v1 *= alpha; v2 *= alpha; v3 *= alpha;
+          if (beta != 0.f) {
+            const u32x2 old = *reinterpret_cast<const u32x2*>(op + d0);
+            v0 += beta * bf16_lo(old[0]); v1 += beta * bf16_hi(old[0]);
+            v2 += beta * bf16_lo(old[1]); v3 += beta * bf16_hi(old[1]);
+          }
+        }
+        const u32x2 pk = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+        *reinterpret_cast<u32x2*>(op + d0) = pk;
+      }
+  }
+}
+
+// One wave: groups sorted by decreasing size (ties: lower id first) and the
+// prefix count of (head, query-tile) items in that order.
+__global__ __launch_bounds__(kWave) void schedule_kernel(const int32_t* __restrict__ cu, int M, int H,
+                                                       AttnSchedule* __restrict__ sched) {
+  __shared__ int order_s[kMaxGroups];
+  const int g = threadIdx.x;
+  const int n = g < M ? cu[g + 1] - cu[g] : -1;
+  if (g < M) {
+    int rank = 0;
+    for (int o = 0; o < M; ++o) {
+      const int no = cu[o + 1] - cu[o];
+      rank += (no > n) || (no == n && o < g);
+    }
+    order_s[rank] = g;
+  }
+  __syncthreads();
+  int tiles = 0;
+  if (g < M) {
+    const int og = order_s[g];
+    sched->order[g] = og;
+    tiles = (cu[og + 1] - cu[og] + kBM - 1) / kBM * H;
+  }
+  // inclusive scan across the wave
+  int incl = tiles;
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int v = __shfl_up(incl, off);
+    if (g >= off) incl += v;
+  }
+  if (g < M) sched->prefix[g + 1] = incl;
+  if (g == 0) sched->prefix[0] = 0;
+}
+
+template <int D, class Rows, bool kStga>
+int launch_attn(const void* Q, const void* K, const void* V, void* O, int64_t row_stride, float scale,
+                float alpha, float beta, Rows rows, int64_t items_bound, hipStream_t st) {
+  const int64_t run = (int64_t)kNumXcd * kXcdRun;
+  const int64_t grid = ceil_div(items_bound, run) * run;
+  if (grid > 0x7fffffff) return MOGA_ERR_SHAPE;
+  attn_kernel<D, Rows, kStga><<<dim3((unsigned)grid), kAttnWaves * kWave, 0, st>>>(
+      static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V),
+      static_cast<uint16_t*>(O), row_stride, scale * 1.4426950408889634f, alpha, beta, rows);
+  MOGA_LAUNCH_CHECK();
+  return MOGA_OK;
+}
+
+}  // namespace
+}  // namespace moga
+
+extern "C" int moga_group_attention(const void* Qp, const void* Kp, const void* Vp, const int32_t* cu_seqlens,
+                                    int64_t N, int32_t H, int32_t D, int32_t M, float softmax_scale, void* Op,
+                                    void* ws, size_t ws_bytes, void* stream) {
+  using namespace moga;
+  if (!Qp || !Kp || !Vp || !cu_seqlens || !Op) return MOGA_ERR_NULL;
+  if (N < 1 || N >= (int64_t(1) << 31) || M < 1 || H < 1 || D < 1) return MOGA_ERR_SHAPE;
+  if (M > kMaxGroups || !valid_head_dims(H, D)) return MOGA_ERR_UNSUPPORTED;
+  const size_t need = moga_workspace_bytes(MOGA_OP_GROUP_ATTENTION, N, M, H, D);
+  if (!ws || ws_bytes < need) return MOGA_ERR_WORKSPACE;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
+  hipStream_t st = as_stream(stream);
+  auto* sched = static_cast<AttnSchedule*>(ws);
+  schedule_kernel<<<1, kWave, 0, st>>>(cu_seqlens, M, H, sched);
+  MOGA_LAUNCH_CHECK();
+  MogaRows rows{cu_seqlens, sched, M, H};
+  const int64_t bound = (ceil_div(N, kBM) + M) * H;
+  if (D == 128) return launch_attn<128, MogaRows, false>(Qp, Kp, Vp, Op, (int64_t)H * D, scale, 1.f, 0.f, rows, bound, st);
+  return launch_attn<64, MogaRows, false>(Qp, Kp, Vp, Op, (int64_t)H * D, scale, 1.f, 0.f, rows, bound, st);
+}
+
+extern "C" int moga_stga_attention(const void* Q, const void* K, const void* V, int32_t T, int32_t Hs, int32_t Ws,
+                                   int32_t win_t, int32_t tile_h, int32_t tile_w, int32_t H, int32_t D,
+                                   float softmax_scale, float alpha, float beta, void* O, void* stream) {
+  using namespace moga;
+  if (!Q || !K || !V || !O) return MOGA_ERR_NULL;
+  if (T < 1 || Hs < 1 || Ws < 1 || win_t < 1 || tile_h < 1 || tile_w < 1 || H < 1 || D < 1) return MOGA_ERR_SHAPE;
+  if (T % win_t || Hs % tile_h || Ws % tile_w) return MOGA_ERR_SHAPE;
+  const int64_t N = (int64_t)T * Hs * Ws;
+  const int64_t gsize = (int64_t)win_t * tile_h * tile_w;
+  if (N >= (int64_t(1) << 31)) return MOGA_ERR_SHAPE;
+  if (gsize > (int64_t(1) << 20) || !valid_head_dims(H, D)) return MOGA_ERR_UNSUPPORTED;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
+  const int tpg = (int)ceil_div(gsize, kBM);
+  const int64_t items = (N / gsize) * H * tpg;
+  if (items > 0x7fffffff) return MOGA_ERR_SHAPE;
+  StgaRows rows{Hs, Ws, win_t, tile_h, tile_w, Hs / tile_h, Ws / tile_w, tpg, H, (int)items};
+  hipStream_t st = as_stream(stream);
+  if (D == 128) return launch_attn<128, StgaRows, true>(Q, K, V, O, (int64_t)H * D, scale, alpha, beta, rows, items, st);
+  return launch_attn<64, StgaRows, true>(Q, K, V, O, (int64_t)H * D, scale, alpha, beta, rows, items, st);
+}

@@ -1,0 +1,188 @@
+// Group permutation: stable counting sort of tokens by group id, then a
+// row gather of Q, K, V into group-contiguous order.
+// Page "MoGA: Mixture-of-Groups Attention for End-to-End Long Video
+// Generation", section "MoGA Pseudocode and Kernel Integration", Algorithm 1
+// step 2 (group 0 first, then group 1, ...; cu_seqlen, max_seqlen and the
+// permute index as by-products).
+//
+// Four launches on the caller's stream, no host round trip:
+//   hist_kernel     per 1024-token block, count tokens of each group (LDS)
+//   scan_kernel     one workgroup: exclusive scan of the [M][blocks] counts in
+//                   group-major order -> each (group, block) base offset,
+//                   cu_seqlens and max_seqlen
+//   scatter_kernel  per block, stable ranks from wave ballots: lanes holding
+//                   the same group id find each other with log2(M) ballots,
+//                   rank = popcount of lower matching lanes; waves of a round
+//                   are ordered through LDS counts -> perm[base + rank] = n
+//   gather_kernel   Qp/Kp/Vp[j] = Q/K/V[perm[j]], whole H*D rows, 16-byte
+//                   lanes, one wave per row copy (HBM-bound stream)
+#include "moga_internal.h"
+
+namespace moga {
+namespace {
+
+constexpr int kSortThreads = 256;
+constexpr int kSortWaves = kSortThreads / kWave;
+
+__global__ __launch_bounds__(kSortThreads) void hist_kernel(const int32_t* __restrict__ gid, int64_t N, int M,
+                                                          int nblk, int32_t* __restrict__ hist) {
+  __shared__ int h[kMaxGroups];
+  if (threadIdx.x < kMaxGroups) h[threadIdx.x] = 0;
+  __syncthreads();
+  const int64_t n0 = (int64_t)blockIdx.x * kSortChunk;
+  for (int i = threadIdx.x; i < kSortChunk; i += kSortThreads) {
+    const int64_t n = n0 + i;
+    if (n < N) atomicAdd(&h[gid[n]], 1);
+  }
+  __syncthreads();
+  if (threadIdx.x < M) hist[(int64_t)threadIdx.x * nblk + blockIdx.x] = h[threadIdx.x];
+}
+
+constexpr int kScanThreads = 1024;
+
+// Exclusive scan over E = M * nblk counts laid out group-major.
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __restrict__ hist, int M, int nblk,
+                                                          int64_t N, int32_t* __restrict__ base,
+                                                          int32_t* __restrict__ cu, int32_t* __restrict__ max_seqlen) {
+  __shared__ int part[kScanThreads];
+  const int64_t E = (int64_t)M * nblk;
+  const int64_t per = (E + kScanThreads - 1) / kScanThreads;
+  const int64_t lo = threadIdx.x * per;
+  const int64_t hi = lo + per < E ? lo + per : E;
+  int s = 0;
+  for (int64_t e = lo; e < hi; ++e) s += hist[e];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  // Hillis-Steele inclusive scan of the per-thread sums
+  for (int off = 1; off < kScanThreads; off <<= 1) {
+    const int v = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int run = threadIdx.x ? part[threadIdx.x - 1] : 0;
+  for (int64_t e = lo; e < hi; ++e) {
+    base[e] = run;
+    if (e % nblk == 0) cu[e / nblk] = run;  // first block of group e / nblk
+    run += hist[e];
+  }
+  if (threadIdx.x == 0) cu[M] = (int32_t)N;
+  __syncthreads();  // makes every cu entry visible to the block
+  if (threadIdx.x < kWave) {  // max group size over M <= 64 entries: wave 0 only
+    int v = 0;
+    if (threadIdx.x < M) v = cu[threadIdx.x + 1] - cu[threadIdx.x];
+    for (int off = 32; off >= 1; off >>= 1) {
+      const int o = __shfl_xor(v, off);
+      v = o > v ? o : v;
+    }
+    if (threadIdx.x == 0) *max_seqlen = v;
+  }
+}
+
+__global__ __launch_bounds__(kSortThreads) void scatter_kernel(const int32_t* __restrict__ gid, int64_t N, int M,
+                                                             int nblk, const int32_t* __restrict__ base,
+                                                             int32_t* __restrict__ perm) {
+  __shared__ int run[kMaxGroups];
+  __shared__ int wcnt[kSortWaves][kMaxGroups];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (threadIdx.x < M) run[threadIdx.x] = base[(int64_t)threadIdx.x * nblk + blockIdx.x];
+  for (int i = threadIdx.x; i < kSortWaves * kMaxGroups; i += kSortThreads) (&wcnt[0][0])[i] = 0;
+  int bits = 0;
+  while ((1 << bits) < M) ++bits;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  __syncthreads();
+
+  const int64_t n0 = (int64_t)blockIdx.x * kSortChunk;
+  for (int r0 = 0; r0 < kSortChunk; r0 += kSortThreads) {
+    const int64_t n = n0 + r0 + threadIdx.x;
+    const bool valid = n < N;
+    const int g = valid ? gid[n] : 0;
+    uint64_t match = __ballot(valid);
+    for (int b = 0; b < bits; ++b) {
+      const bool bit = (g >> b) & 1;
+      const uint64_t ones = __ballot(valid && bit);
+      match &= bit ? ones : ~ones;
+    }
+    const int rank = __popcll(match & lt_mask);
+    if (valid && rank == 0) wcnt[wave][g] = __popcll(match);
+    __syncthreads();
+    if (valid) {
+      int off = run[g] + rank;
+      for (int w = 0; w < wave; ++w) off += wcnt[w][g];
+      perm[off] = (int32_t)n;
+    }
+    __syncthreads();
+    if (threadIdx.x < M) {
+      int add = 0;
+      for (int w = 0; w < kSortWaves; ++w) {
+        add += wcnt[w][threadIdx.x];
+        wcnt[w][threadIdx.x] = 0;
+      }
+      run[threadIdx.x] += add;
+    }
+    __syncthreads();
+  }
+}
+
+constexpr int kGatherWaves = 4;
+constexpr int kGatherRows = 16;  // rows per workgroup
+
+// Qp/Kp/Vp[j] = Q/K/V[perm[j]]; rows are `chunks` 16-byte pieces long.
+__global__ __launch_bounds__(kGatherWaves * kWave) void gather_kernel(
+    const int32_t* __restrict__ perm, int64_t N, int chunks, const u32x4* __restrict__ Q,
+    const u32x4* __restrict__ K, const u32x4* __restrict__ V, u32x4* __restrict__ Qp, u32x4* __restrict__ Kp,
+    u32x4* __restrict__ Vp) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t j0 = (int64_t)blockIdx.x * kGatherRows;
+  for (int rr = wave; rr < kGatherRows; rr += kGatherWaves) {
+    const int64_t j = j0 + rr;
+    if (j >= N) break;
+    const int64_t src = (int64_t)perm[j] * chunks, dst = j * chunks;
+    for (int c = lane; c < chunks; c += kWave) {
+      const u32x4 a = __builtin_nontemporal_load(Q + src + c);
+      const u32x4 b = __builtin_nontemporal_load(K + src + c);
+      const u32x4 d = __builtin_nontemporal_load(V + src + c);
+      __builtin_nontemporal_store(a, Qp + dst + c);
+      __builtin_nontemporal_store(b, Kp + dst + c);
+      __builtin_nontemporal_store(d, Vp + dst + c);
+    }
+  }
+}
+
+}  // namespace
+}  // namespace moga
+
+extern "C" int moga_permute(const int32_t* group_id, const void* Q, const void* K, const void* V, int64_t N,
+                            int32_t H, int32_t D, int32_t M, void* Qp, void* Kp, void* Vp, int32_t* perm,
+                            int32_t* cu_seqlens, int32_t* max_seqlen, void* ws, size_t ws_bytes, void* stream) {
+  using namespace moga;
+  if (!group_id || !perm || !cu_seqlens || !max_seqlen) return MOGA_ERR_NULL;
+  const bool any_rows = Q || K || V || Qp || Kp || Vp;
+  const bool all_rows = Q && K && V && Qp && Kp && Vp;
+  if (any_rows && !all_rows) return MOGA_ERR_NULL;
+  if (N < 1 || N >= (int64_t(1) << 31) || M < 1) return MOGA_ERR_SHAPE;
+  if (M > kMaxGroups) return MOGA_ERR_UNSUPPORTED;
+  if (all_rows && !valid_head_dims(H, D)) return (H < 1 || D < 1) ? MOGA_ERR_SHAPE : MOGA_ERR_UNSUPPORTED;
+  const size_t need = moga_workspace_bytes(MOGA_OP_PERMUTE, N, M, H, D);
+  if (!ws || ws_bytes < need) return MOGA_ERR_WORKSPACE;
+
+  hipStream_t st = as_stream(stream);
+  const int nblk = (int)sort_blocks(N);
+  int32_t* hist = static_cast<int32_t*>(ws);
+  int32_t* base = hist + (size_t)M * nblk;
+  hist_kernel<<<nblk, kSortThreads, 0, st>>>(group_id, N, M, nblk, hist);
+  MOGA_LAUNCH_CHECK();
+  scan_kernel<<<1, kScanThreads, 0, st>>>(hist, M, nblk, N, base, cu_seqlens, max_seqlen);
+  MOGA_LAUNCH_CHECK();
+  scatter_kernel<<<nblk, kSortThreads, 0, st>>>(group_id, N, M, nblk, base, perm);
+  MOGA_LAUNCH_CHECK();
+  if (all_rows) {
+    const int chunks = H * D / 8;
+    const int64_t blocks = ceil_div(N, kGatherRows);
+    gather_kernel<<<dim3((unsigned)blocks), kGatherWaves * kWave, 0, st>>>(
+        perm, N, chunks, static_cast<const u32x4*>(Q), static_cast<const u32x4*>(K), static_cast<const u32x4*>(V),
+        static_cast<u32x4*>(Qp), static_cast<u32x4*>(Kp), static_cast<u32x4*>(Vp));
+    MOGA_LAUNCH_CHECK();
+  }
+  return MOGA_OK;
+}

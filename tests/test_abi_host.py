@@ -1,0 +1,124 @@
+"""The C ABI on a host without a GPU: the library loads, exports every symbol
+include/moga.h declares, sizes workspaces, and rejects bad arguments on the
+host before launching anything (no compute call is made here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moga.h")
+LIB = os.path.join(ROOT, "sparse_attention_long_router_amd", "libmoga.so")
+
+OK, ENULL, ESHAPE, EUNSUP, EWS, EHIP = 0, -1, -2, -3, -4, -5
+FAKE = ctypes.c_void_p(4096)  # never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from sparse_attention_long_router_amd import build
+        build.build(verbose=False)
+    from sparse_attention_long_router_amd import _lib
+    return _lib.LIB
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moga_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_symbols()
+    assert len(names) == 8, names
+    for n in names:
+        assert hasattr(lib, n), n
+    from sparse_attention_long_router_amd import _lib
+    assert sorted(_lib.SIGNATURES) == names
+
+
+def test_strerror_and_version(lib):
+    for code in (OK, ENULL, ESHAPE, EUNSUP, EWS, EHIP):
+        assert lib.moga_strerror(code)
+    assert lib.moga_strerror(-99) == b"unknown status"
+    assert lib.moga_version() >= 100
+
+
+def test_workspace_sizes(lib):
+    ws = lib.moga_workspace_bytes
+    assert ws(0, 1000, 4, 2, 64) == 0                      # route needs none
+    assert ws(3, 1000, 4, 2, 64) == 0 and ws(4, 1000, 4, 2, 64) == 0
+    n = ws(1, 190320, 16, 12, 128)
+    nblk = -(-190320 // 1024)
+    assert n >= 2 * 16 * nblk * 4 and n % 256 == 0
+    assert ws(2, 190320, 16, 12, 128) >= (64 + 65) * 4
+    assert ws(1, 0, 16, 12, 128) == 0 and ws(1, 10, 65, 1, 64) == 0 and ws(1, 10, 0, 1, 64) == 0
+
+
+def test_route_argument_errors(lib):
+    r = lib.moga_route
+    assert r(None, FAKE, None, 10, 64, 4, FAKE, FAKE, None) == ENULL
+    assert r(FAKE, FAKE, None, 10, 64, 4, None, FAKE, None) == ENULL
+    assert r(FAKE, FAKE, None, 0, 64, 4, FAKE, FAKE, None) == ESHAPE
+    assert r(FAKE, FAKE, None, 1 << 31, 64, 4, FAKE, FAKE, None) == ESHAPE
+    assert r(FAKE, FAKE, None, 10, 64, 0, FAKE, FAKE, None) == ESHAPE
+    assert r(FAKE, FAKE, None, 10, 64, 65, FAKE, FAKE, None) == EUNSUP
+    assert r(FAKE, FAKE, None, 10, 48, 4, FAKE, FAKE, None) == EUNSUP
+
+
+def test_permute_argument_errors(lib):
+    p = lib.moga_permute
+    good_ws = lib.moga_workspace_bytes(1, 100, 4, 2, 128)
+    args = dict(g=FAKE, Q=FAKE, K=FAKE, V=FAKE, N=100, H=2, D=128, M=4, Qp=FAKE, Kp=FAKE, Vp=FAKE,
+                perm=FAKE, cu=FAKE, mx=FAKE, ws=FAKE, nb=good_ws)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return p(a["g"], a["Q"], a["K"], a["V"], a["N"], a["H"], a["D"], a["M"], a["Qp"], a["Kp"], a["Vp"],
+                 a["perm"], a["cu"], a["mx"], a["ws"], a["nb"], None)
+
+    assert call(g=None) == ENULL
+    assert call(cu=None) == ENULL
+    assert call(Kp=None) == ENULL                    # some but not all row tensors
+    assert call(N=0) == ESHAPE
+    assert call(M=0) == ESHAPE
+    assert call(M=65) == EUNSUP
+    assert call(D=96) == EUNSUP
+    assert call(H=0) == ESHAPE
+    assert call(H=128, D=128) == EUNSUP              # H*D > 8192
+    assert call(ws=None) == EWS
+    assert call(nb=good_ws - 1) == EWS
+
+
+def test_attention_argument_errors(lib):
+    a = lib.moga_group_attention
+    nb = lib.moga_workspace_bytes(2, 100, 4, 2, 128)
+    assert a(None, FAKE, FAKE, FAKE, 100, 2, 128, 4, 0.0, FAKE, FAKE, nb, None) == ENULL
+    assert a(FAKE, FAKE, FAKE, FAKE, 100, 2, 128, 4, 0.0, None, FAKE, nb, None) == ENULL
+    assert a(FAKE, FAKE, FAKE, FAKE, 0, 2, 128, 4, 0.0, FAKE, FAKE, nb, None) == ESHAPE
+    assert a(FAKE, FAKE, FAKE, FAKE, 100, 2, 80, 4, 0.0, FAKE, FAKE, nb, None) == EUNSUP
+    assert a(FAKE, FAKE, FAKE, FAKE, 100, 2, 128, 70, 0.0, FAKE, FAKE, nb, None) == EUNSUP
+    assert a(FAKE, FAKE, FAKE, FAKE, 100, 2, 128, 4, 0.0, FAKE, None, nb, None) == EWS
+    assert a(FAKE, FAKE, FAKE, FAKE, 100, 2, 128, 4, 0.0, FAKE, FAKE, nb - 1, None) == EWS
+
+
+def test_unpermute_argument_errors(lib):
+    u = lib.moga_unpermute
+    assert u(None, FAKE, FAKE, 10, 2, 64, 0.0, FAKE, None) == ENULL
+    assert u(FAKE, FAKE, None, 10, 2, 64, 0.0, FAKE, None) == ENULL
+    assert u(FAKE, FAKE, FAKE, -1, 2, 64, 0.0, FAKE, None) == ESHAPE
+    assert u(FAKE, FAKE, FAKE, 10, 2, 32, 0.0, FAKE, None) == EUNSUP
+
+
+def test_stga_argument_errors(lib):
+    s = lib.moga_stga_attention
+    assert s(None, FAKE, FAKE, 6, 30, 52, 3, 30, 26, 2, 128, 0.0, 1.0, 0.0, FAKE, None) == ENULL
+    assert s(FAKE, FAKE, FAKE, 6, 30, 52, 4, 30, 26, 2, 128, 0.0, 1.0, 0.0, FAKE, None) == ESHAPE  # 4 !| 6
+    assert s(FAKE, FAKE, FAKE, 6, 30, 52, 3, 7, 26, 2, 128, 0.0, 1.0, 0.0, FAKE, None) == ESHAPE   # 7 !| 30
+    assert s(FAKE, FAKE, FAKE, 6, 30, 52, 3, 30, 25, 2, 128, 0.0, 1.0, 0.0, FAKE, None) == ESHAPE  # 25 !| 52
+    assert s(FAKE, FAKE, FAKE, 0, 30, 52, 1, 30, 26, 2, 128, 0.0, 1.0, 0.0, FAKE, None) == ESHAPE
+    assert s(FAKE, FAKE, FAKE, 6, 30, 52, 3, 30, 26, 2, 100, 0.0, 1.0, 0.0, FAKE, None) == EUNSUP
+    assert s(FAKE, FAKE, FAKE, 2048, 1024, 1024, 2048, 1024, 1024, 1, 64, 0.0, 1.0, 0.0, FAKE, None) == ESHAPE

@@ -1,0 +1,166 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Integer results (group ids, permutation, cu_seqlens, max_seqlen, gathered rows)
+must be bit-exact; float32 gates within GATE_RTOL; bf16 outputs within the
+max-abs / mean-abs / relative-Frobenius bars of tests/parity.py.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import assert_gate_close, assert_output_close
+from workloads import get_workload, make_inputs, sample_rows
+from workloads.gen import to_numpy_f32
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def moga():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_attention_long_router_amd as m
+    return m
+
+
+def _np(t):
+    return to_numpy_f32(t)
+
+
+def _inputs(name, seed=None, device="cpu", **over):
+    """Draw on the CPU (reproducible) and move to the GPU."""
+    inp = make_inputs(get_workload(name), device=device, seed=seed, **over)
+    return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+
+
+def _full_check(moga, inp, bias=None, label=""):
+    wl = inp["workload"]
+    X, Wr, Q, K, V = (inp[k] for k in ("X", "Wr", "Q", "K", "V"))
+    M = Wr.shape[0]
+    print(f"[parity] {label} N={X.shape[0]} H={Q.shape[1]} D={Q.shape[2]} M={M}", flush=True)
+    gid, gate = moga.moga_route(X, Wr, bias)
+    p = moga.moga_permute(gid, M, Q, K, V)
+    Op = moga.moga_group_attention(p["Qp"], p["Kp"], p["Vp"], p["cu_seqlens"])
+    O = moga.moga_unpermute(Op, p["perm"], gate)
+    torch.cuda.synchronize()
+
+    Xn, Wn, Qn, Kn, Vn = (_np(t) for t in (X, Wr, Q, K, V))
+    bn = None if bias is None else bias.cpu().numpy()
+    ref = oracle.moga_forward(Xn, Wn, Qn, Kn, Vn, M, bias=bn)
+    np.testing.assert_array_equal(gid.cpu().numpy(), ref["group_id"])
+    assert_gate_close(gate.cpu().numpy(), ref["gate"])
+    np.testing.assert_array_equal(p["perm"].cpu().numpy(), ref["perm"])
+    np.testing.assert_array_equal(p["cu_seqlens"].cpu().numpy(), ref["cu_seqlens"])
+    assert int(p["max_seqlen"].item()) == ref["max_seqlen"]
+    perm = p["perm"].long()
+    for a, b in ((p["Qp"], Q), (p["Kp"], K), (p["Vp"], V)):
+        assert torch.equal(a, b[perm])
+    e_attn = assert_output_close(_np(Op), ref["Op"], "Op")
+    e_out = assert_output_close(_np(O), ref["O"], "O")
+    print(f"[parity] {label} Op {e_attn} O {e_out}", flush=True)
+    return gid, gate, p, Op, O, ref
+
+
+def test_tiny_workload(moga):
+    _full_check(moga, _inputs("tiny"), label="tiny")
+
+
+@pytest.mark.parametrize("N,H,D,M", [
+    (6000, 4, 128, 8),      # several 128-query tiles and 64-key tiles, ragged tails
+    (777, 2, 128, 1),       # one group: full attention
+    (3001, 1, 64, 64),      # many small groups
+    (1, 3, 128, 4),         # a single token
+    (5, 2, 64, 3),          # fewer tokens than a tile
+    (4097, 3, 128, 16),
+])
+def test_shapes(moga, N, H, D, M):
+    _full_check(moga, _inputs("wan13b_21f", N=N, H=H, D=D, M=M, d_model=256), label=f"shape{N}")
+
+
+def test_skewed_with_bias_and_empty_groups(moga):
+    inp = _inputs("clip30s_122f", N=5000, H=2, D=128, M=6, d_model=512)
+    # bias pushes most tokens into group 2 and empties group 5
+    bias = torch.tensor([0.0, 0.0, 6.0, 0.0, 0.0, -60.0], device=DEV)
+    gid, *_ = _full_check(moga, inp, bias=bias, label="skew")
+    counts = np.bincount(gid.cpu().numpy(), minlength=6)
+    assert counts[5] == 0 and counts[2] > 0.5 * 5000
+
+
+def test_attention_deterministic(moga):
+    inp = _inputs("wan13b_21f", N=3000, H=2, D=128, M=4, d_model=256)
+    gid, gate = moga.moga_route(inp["X"], inp["Wr"])
+    p = moga.moga_permute(gid, 4, inp["Q"], inp["K"], inp["V"])
+    a = moga.moga_group_attention(p["Qp"], p["Kp"], p["Vp"], p["cu_seqlens"])
+    b = moga.moga_group_attention(p["Qp"], p["Kp"], p["Vp"], p["cu_seqlens"])
+    assert torch.equal(a, b)
+
+
+def test_unpermute_accumulate(moga):
+    inp = _inputs("wan13b_21f", N=2500, H=2, D=64, M=5, d_model=128)
+    gid, gate = moga.moga_route(inp["X"], inp["Wr"])
+    p = moga.moga_permute(gid, 5, inp["Q"], inp["K"], inp["V"])
+    prev = inp["V"].clone()
+    O = moga.moga_unpermute(p["Qp"], p["perm"], gate, beta=0.5, O=prev)
+    torch.cuda.synchronize()
+    ref = oracle.unpermute(_np(p["Qp"]), p["perm"].cpu().numpy(), gate.cpu().numpy(), 0.5, _np(inp["V"]))
+    d = np.abs(_np(O) - ref) / np.maximum(np.abs(ref), 1e-30)
+    assert d.max() <= 2.0 ** -8  # one bf16 rounding of an exact float32 expression
+
+
+@pytest.mark.parametrize("T,Hs,Ws,win_t,th,tw,H,D,alpha,beta", [
+    (6, 6, 10, 3, 3, 5, 2, 128, 1.0, 0.0),     # groups of 45: one partial tile
+    (4, 30, 52, 2, 30, 26, 1, 128, 0.5, 0.5),  # Wan-like frames, groups of 1560
+    (3, 8, 8, 1, 8, 8, 2, 64, 1.0, 1.0),
+])
+def test_stga(moga, T, Hs, Ws, win_t, th, tw, H, D, alpha, beta):
+    N = T * Hs * Ws
+    print(f"[parity] stga N={N} geo={T, Hs, Ws, win_t, th, tw} H={H} D={D}", flush=True)
+    inp = _inputs("tiny", N=N, H=H, D=D, M=2)
+    Q, K, V = inp["Q"], inp["K"], inp["V"]
+    O = V.clone() if beta != 0 else None
+    out = moga.moga_stga_attention(Q, K, V, T, Hs, Ws, win_t, th, tw, alpha=alpha, beta=beta, O=O)
+    torch.cuda.synchronize()
+    ref = oracle.stga_attention(_np(Q), _np(K), _np(V), T, Hs, Ws, win_t, th, tw, 1 / math.sqrt(D),
+                                alpha=alpha, beta=beta, O_prev=_np(V))
+    assert_output_close(_np(out), ref, "STGA")
+
+
+# ---------------------------------------------------------------------------
+# Full workload sizes, in the launch configuration the benchmark times
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["wan13b_21f", "clip30s_122f", "wan14b_122f", "minute_372f"])
+def test_full_size_sampled(moga, name):
+    wl = get_workload(name)
+    print(f"[parity] full {name} N={wl.N} d={wl.d_model} H={wl.H} M={wl.M}", flush=True)
+    inp = make_inputs(wl, device=DEV)
+    X, Wr, Q, K, V = (inp[k] for k in ("X", "Wr", "Q", "K", "V"))
+    fwd = moga.MogaForward(wl.N, wl.d_model, wl.H, wl.D, wl.M, DEV, stga=wl.stga)
+    O = fwd(X, Wr, Q, K, V)
+    torch.cuda.synchronize()
+
+    Xn, Wn = _np(X), _np(Wr)
+    g_ref, gate_ref, _ = oracle.route(Xn, Wn)
+    np.testing.assert_array_equal(fwd.group_id.cpu().numpy(), g_ref)
+    assert_gate_close(fwd.gate.cpu().numpy(), gate_ref)
+    perm_ref, cu_ref, mx_ref = oracle.permute(g_ref, wl.M)
+    np.testing.assert_array_equal(fwd.perm.cpu().numpy(), perm_ref)
+    np.testing.assert_array_equal(fwd.cu_seqlens.cpu().numpy(), cu_ref)
+    assert int(fwd.max_seqlen.item()) == mx_ref
+
+    rows = sample_rows(g_ref, wl.M, per_group=3, seed=wl.seed)
+    Qn, Kn, Vn = _np(Q), _np(K), _np(V)
+    want = oracle.moga_output_rows(Xn, Wn, Qn, Kn, Vn, wl.M, rows, routed=(g_ref, gate_ref))
+    if wl.stga is not None:
+        s = wl.stga
+        ids = oracle.stga_group_ids(s["T"], s["Hs"], s["Ws"], s["win_t"], s["tile_h"], s["tile_w"])
+        want = want + oracle.stga_attention_rows(Qn, Kn, Vn, ids, 1 / math.sqrt(wl.D), rows)
+    got = _np(O[torch.from_numpy(rows).to(DEV)])
+    e = assert_output_close(got, want, f"{name} sampled O")
+    print(f"[parity] full {name}: {rows.size} rows, {e}", flush=True)
