@@ -1,0 +1,224 @@
+"""Benchmark of the MoGA forward hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one pass of the whole path over one synthetic batch already resident
+in HBM: route -> permute (sort + Q/K/V gather) -> group attention -> gated
+unpermute (-> STGA sum for workloads that have it).  Prints ONE JSON line.
+
+value = effective TFLOP/s of the whole step, counting only within-group
+attention FLOPs 4*H*D*sum_g n_g^2 (plus the STGA windows when present);
+tokens_per_s = N / step time.  The roofline object covers the dominant kernel
+(group attention), timed live with HIP events on the stream it runs on.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+METRIC = "MoGA attn effective TFLOP/s + tokens/s per layer at N≈190k, %MFMA peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_group_attention_clip30s_122f.json")
+ATTN_SOURCE = os.path.join(ROOT, "sparse_attention_long_router_amd", "csrc", "attention.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=800, help="sampled query rows per group for the oracle")
+    return ap.parse_args()
+
+
+def attn_flops(counts, H, D):
+    return 4.0 * H * D * float(sum(int(c) ** 2 for c in counts))
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_entry(launch_flops_key):
+    """HBM bytes per attention launch from the committed counter summary, or
+    None when the kernel source changed after the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("attention_source_sha256_16") != source_hash(ATTN_SOURCE):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, wl, counts, rows_per_group):
+    """The oracle, untuned, on a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle
+    from workloads.gen import sample_rows, to_numpy_f32
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+
+    X, Wr, Q, K, V = (to_numpy_f32(inp[k]) for k in ("X", "Wr", "Q", "K", "V"))
+    t0 = time.perf_counter()
+    g, gate, _ = oracle.route(X, Wr)
+    perm, cu, _ = oracle.permute(g, wl.M)
+    t_route = time.perf_counter() - t0
+    # sampled attention rows: first/last plus random rows of every group, all heads
+    rows = sample_rows(g, wl.M, rows_per_group, seed=wl.seed)
+    t1 = time.perf_counter()
+    oracle.moga_output_rows(X, Wr, Q, K, V, wl.M, rows, routed=(g, gate))
+    t_attn = time.perf_counter() - t1
+    n = np.bincount(g, minlength=wl.M)
+    sample_flops = 4.0 * wl.H * wl.D * float(sum(n[g[r]] for r in rows))
+    total_flops = attn_flops(counts, wl.H, wl.D)
+    t_full = t_route + t_attn * total_flops / sample_flops
+    return {
+        "value": total_flops / t_full / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"route + permute over all {wl.N} tokens ({t_route:.2f} s); attention of {rows.size} "
+                   f"sampled query rows (first, last and {rows_per_group} random per group) x {wl.H} heads "
+                   f"({t_attn:.2f} s, {sample_flops / 1e9:.1f} GFLOP), extrapolated by FLOPs to the full step "
+                   f"({t_full:.1f} s); float64 NumPy, {len(os.sched_getaffinity(0))} cores visible"),
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not supported. "
+              "Multi-GPU sharding is described in DESIGN.md, not implemented.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_attention_long_router_amd as moga
+    from workloads import get_workload, make_inputs
+    from workloads.configs import BENCH_WORKLOAD
+
+    wl = get_workload(args.workload or BENCH_WORKLOAD)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = make_inputs(wl, device=dev)
+    X, Wr, Q, K, V = (inp[k] for k in ("X", "Wr", "Q", "K", "V"))
+    fwd = moga.MogaForward(wl.N, wl.d_model, wl.H, wl.D, wl.M, dev, stga=wl.stga)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        # same five library calls as MogaForward.__call__, with events between stages
+        if ev is not None:
+            ev[0].record(stream)
+        moga.moga_route(X, Wr, None, fwd.group_id, fwd.gate)
+        if ev is not None:
+            ev[1].record(stream)
+        moga.moga_permute(fwd.group_id, wl.M, Q, K, V, fwd.Qp, fwd.Kp, fwd.Vp, fwd.perm, fwd.cu_seqlens,
+                          fwd.max_seqlen, fwd.ws_perm)
+        if ev is not None:
+            ev[2].record(stream)
+        moga.moga_group_attention(fwd.Qp, fwd.Kp, fwd.Vp, fwd.cu_seqlens, 0.0, fwd.Op, fwd.ws_attn)
+        if ev is not None:
+            ev[3].record(stream)
+        moga.moga_unpermute(fwd.Op, fwd.perm, fwd.gate, 0.0, fwd.O)
+        if ev is not None:
+            ev[4].record(stream)
+        if wl.stga is not None:
+            s = wl.stga
+            moga.moga_stga_attention(Q, K, V, s["T"], s["Hs"], s["Ws"], s["win_t"], s["tile_h"], s["tile_w"],
+                                     0.0, 1.0, 1.0, fwd.O)
+        if ev is not None:
+            ev[5].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    stages = ["route", "permute", "group_attention", "unpermute", "stga"]
+    breakdown = {s: sum(e[k].elapsed_time(e[k + 1]) for e in evs) / args.steps for k, s in enumerate(stages)}
+    if wl.stga is None:
+        breakdown.pop("stga")
+
+    counts = (fwd.cu_seqlens[1:] - fwd.cu_seqlens[:-1]).cpu().tolist()
+    flops_moga = attn_flops(counts, wl.H, wl.D)
+    flops_stga = 0.0
+    if wl.stga is not None:
+        s = wl.stga
+        gsize = s["win_t"] * s["tile_h"] * s["tile_w"]
+        flops_stga = 4.0 * wl.H * wl.D * gsize * gsize * (wl.N // gsize)
+    step_flops = flops_moga + flops_stga
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    attn_ms = breakdown["group_attention"]
+    achieved = flops_moga / (attn_ms * 1e-3) / 1e12
+
+    traffic = traffic_entry(None)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "kernel": "attn_kernel (moga_group_attention)", "launch_ms": round(attn_ms, 4),
+                "flops_per_launch": flops_moga}
+    mean = wl.N / wl.M
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian-mixture tokens, random-init router and Q/K/V projections)",
+        "config": {"workload": wl.name, "N": wl.N, "d_model": wl.d_model, "H": wl.H, "D": wl.D, "M": wl.M,
+                   "group_max_over_mean": round(max(counts) / mean, 3),
+                   "skew_sum_n2_over_uniform": round(sum(c * c for c in counts) / (wl.N * mean), 3),
+                   "stga": wl.stga},
+        "tokens_per_s": round(wl.N / (ms_per_step * 1e-3), 1),
+        "mfma_frac_step": round(value / PEAK_BF16_TFLOPS, 4),
+        "breakdown_ms": {k: round(v, 4) for k, v in breakdown.items()},
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    hbm = {  # algorithmic bytes per launch of the HBM-bound stages
+        "route": wl.N * (2 * wl.d_model + 8) + 2 * wl.M * wl.d_model,
+        "permute": wl.N * (12 * wl.H * wl.D + 16),
+        "unpermute": wl.N * (4 * wl.H * wl.D + 12),
+    }
+    out["hbm_gbs"] = {k: round(b / (breakdown[k] * 1e-3) / 1e9, 1) for k, b in hbm.items()}
+    out["hbm_frac"] = {k: round(v / PEAK_HBM_GBS, 4) for k, v in out["hbm_gbs"].items()}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, wl, counts, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -29,7 +29,7 @@ namespace moga {
 namespace {
 
 constexpr int kAttnWaves = 4;
-constexpr int kQueriesPerWave = 32;
+constexpr int kQueriesPerWave = 64;
 constexpr int kBM = kAttnWaves * kQueriesPerWave;  // queries per workgroup
 constexpr int kBN = 64;                             // keys per LDS tile
 constexpr int kXcdRun = 8;                          // consecutive items per XCD
@@ -102,16 +102,111 @@ struct StgaRows {
 __device__ __forceinline__ int kswz(int r, int cpr) { return r & (cpr - 1); }
 __device__ __forceinline__ int vswz(int r, int cpr) { return ((r & 3) << 2) & (cpr - 1); }
 
+typedef __attribute__((address_space(1))) void global_void;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Softmax bookkeeping of one 32-query block (one query per lane; the two wave
+// halves hold the same query and exchange one value).
+struct RowState {
+  float m_used;  // exponent offset in use (log2 domain)
+  float l;       // this lane's share of the denominator
+};
+
+// Issue one K/V tile (kBN rows starting at group-local key k0) into LDS with
+// 16-byte direct-to-LDS loads.  Lane i of a load lands at LDS base + 16*i, so
+// the swizzle is applied on the source side: the lane writing physical chunk p
+// of row r fetches logical chunk p ^ swz(r).  Rows past the group end repeat
+// the last row (finite data; their scores are masked).
+template <int D, class Rows>
+__device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                                           uint16_t* Ks, uint16_t* Vs, const Rows& rows, const Work& w,
+                                           int64_t row_stride, int64_t hoff, int k0, int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int LOADS = kBN * CPR / (kAttnWaves * kWave);  // per wave, per tensor
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) {
+    const int q = (wave * LOADS + j) * kWave + lane;  // chunk index inside the tile
+    const int r = q / CPR, p = q % CPR;
+    int key = k0 + r;
+    key = key < w.len ? key : w.len - 1;
+    const int64_t base = rows.row(w, key) * row_stride + hoff;
+    const int lds_off = (wave * LOADS + j) * kWave * 8;  // uint16 elements, wave-uniform
+    __builtin_amdgcn_global_load_lds((global_void*)(K + base + (p ^ kswz(r, CPR)) * 8), (lds_void*)(Ks + lds_off),
+                                     16, 0, 0);
+    __builtin_amdgcn_global_load_lds((global_void*)(V + base + (p ^ vswz(r, CPR)) * 8), (lds_void*)(Vs + lds_off),
+                                     16, 0, 0);
+  }
+}
+
+// S^T for one 32-key block kb of the tile and both query blocks of the wave:
+// reg r of s[b] is key kb*32 + 8*(r/4) + 4*hh + r%4, query c of block b.
+template <int D>
+__device__ __forceinline__ void qk_block(const uint16_t* Ks, const bf16x8 (&qf)[2][D / 16], int kb, int c, int hh,
+                                         f32x16 (&s)[2]) {
+  constexpr int CPR = D / 8;
+  s[0] = f32x16{};
+  s[1] = f32x16{};
+  const int krow = kb * 32 + c;
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) {
+    const int ch = 2 * st + hh;
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + krow * D + (ch ^ kswz(krow, CPR)) * 8);
+    s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][st], s[0], 0, 0, 0);
+    s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[1][st], s[1], 0, 0, 0);
+  }
+}
+
+// Online softmax of one query block over the 64 keys of a tile (s0: keys
+// 0-31, s1: keys 32-63), turning the scores into bf16 P^T operands.  The
+// accumulator is rescaled only when the row max grows by more than 2^kTau.
+constexpr float kTau = 8.0f;
+template <int DBLK>
+__device__ __forceinline__ void softmax_block(f32x16& s0, f32x16& s1, RowState& st, f32x16 (&o)[DBLK],
+                                              float scale_log2, bf16x8 (&pb)[4]) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = mx * scale_log2;
+  const bool need = m_new > st.m_used + kTau;
+  if (__builtin_amdgcn_read_exec() & __ballot(need)) {  // wave-uniform
+    const float target = need ? m_new : st.m_used;
+    const float corr = __builtin_amdgcn_exp2f(st.m_used - target);
+    st.m_used = target;
+    st.l *= corr;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) o[db] *= corr;
+  }
+  float rs = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(s0[r], scale_log2, -st.m_used));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(s1[r], scale_log2, -st.m_used));
+    s0[r] = p0;
+    s1[r] = p1;
+    rs += p0 + p1;
+  }
+  st.l += rs;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      pb[t][j] = (__bf16)s0[8 * t + j];
+      pb[2 + t][j] = (__bf16)s1[8 * t + j];
+    }
+}
+
 template <int D, class Rows, bool kStga>
 __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, int64_t row_stride, float scale_log2, float alpha, float beta, Rows rows) {
-  constexpr int CPR = D / 8;       // 16-byte chunks per row
-  constexpr int KSTEPS = D / 16;   // MFMA k-steps over the head dimension
-  constexpr int DBLK = D / 32;     // 32-wide output blocks
-  constexpr int STAGE_ITERS = kBN * CPR / (kAttnWaves * kWave);
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[kBN * D];
+  constexpr int CPR = D / 8;
+  constexpr int KSTEPS = D / 16;
+  constexpr int DBLK = D / 32;
+  __shared__ __attribute__((aligned(1024))) uint16_t Ks0[kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vs0[kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Ks1[kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vs1[kBN * D];
 
   Work w;
   if (!rows.decode(xcd_remap(blockIdx.x, kXcdRun), w)) return;  // uniform per block
@@ -119,58 +214,47 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, c = lane & 31;
   const int64_t hoff = (int64_t)w.head * D;
+  const int ntiles = (w.len + kBN - 1) / kBN;
 
-  // ---- this lane's query and its Q fragment (B operand of S^T = K Q^T)
-  const int qi = w.q0 + wave * kQueriesPerWave + c;
-  const bool qvalid = qi < w.len;
-  const int64_t qrow = rows.row(w, qvalid ? qi : w.len - 1);
-  bf16x8 qf[KSTEPS];
-  {
-    const uint16_t* qp = Q + qrow * row_stride + hoff + 8 * hh;
+  issue_tile<D>(K, V, Ks0, Vs0, rows, w, row_stride, hoff, 0, wave, lane);
+
+  // this lane's two queries (blocks b = 0, 1) and their Q fragments
+  int64_t qrow[2];
+  bool qvalid[2];
+  bf16x8 qf[2][KSTEPS];
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
+  for (int b = 0; b < 2; ++b) {
+    const int qi = w.q0 + wave * kQueriesPerWave + b * 32 + c;
+    qvalid[b] = qi < w.len;
+    qrow[b] = rows.row(w, qvalid[b] ? qi : w.len - 1);
+    const uint16_t* qp = Q + qrow[b] * row_stride + hoff + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) qf[b][s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
   }
 
-  f32x16 o[DBLK];
+  f32x16 o[2][DBLK];
 #pragma unroll
-  for (int db = 0; db < DBLK; ++db) o[db] = f32x16{};
-  float m_run = -INFINITY;  // running max of the scaled (log2-domain) scores
-  float l_run = 0.f;        // this lane's share of the running denominator
-
-  // tr-read roles (see the operand map in the header comment)
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) o[b][db] = f32x16{};
+  RowState rs[2] = {{-INFINITY, 0.f}, {-INFINITY, 0.f}};
   const int tr_r = (lane & 15) >> 2, tr_q = lane & 3, tr_g = (lane >> 4) & 1;
 
-  for (int k0 = 0; k0 < w.len; k0 += kBN) {
-    // ---- stage K, V rows k0 .. k0+63 (zero rows past the group end)
-#pragma unroll
-    for (int it = 0; it < STAGE_ITERS; ++it) {
-      const int idx = it * (kAttnWaves * kWave) + tid;
-      const int r = idx / CPR, ch = idx % CPR;
-      const int key = k0 + r;
-      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (key < w.len) {
-        const int64_t off = rows.row(w, key) * row_stride + hoff + ch * 8;
-        kv = *reinterpret_cast<const u32x4*>(K + off);
-        vv = *reinterpret_cast<const u32x4*>(V + off);
-      }
-      *reinterpret_cast<u32x4*>(Ks + r * D + (ch ^ kswz(r, CPR)) * 8) = kv;
-      *reinterpret_cast<u32x4*>(Vs + r * D + (ch ^ vswz(r, CPR)) * 8) = vv;
-    }
-    __syncthreads();
+  auto tile = [&](const uint16_t* Ks, const uint16_t* Vs, uint16_t* Kn, uint16_t* Vn, int t) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile t have landed
+    __syncthreads();                // ... and every wave's; tile t-1 is fully consumed
+    if (t + 1 < ntiles) issue_tile<D>(K, V, Kn, Vn, rows, w, row_stride, hoff, (t + 1) * kBN, wave, lane);
+    const int k0 = t * kBN;
 
-    // ---- S^T = K Q^T: two 32-key blocks; reg r of block kb is key
-    //      kb*32 + 8*(r/4) + 4*hh + r%4 of this tile, query c
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      const int krow = kb * 32 + c;
-#pragma unroll
-      for (int st = 0; st < KSTEPS; ++st) {
-        const int ch = 2 * st + hh;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + krow * D + (ch ^ kswz(krow, CPR)) * 8);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[kb], 0, 0, 0);
-      }
+    f32x16 sA[2], sB[2];  // [query block][32-key block]
+    {
+      f32x16 s[2];
+      qk_block<D>(Ks, qf, 0, c, hh, s);
+      sA[0] = s[0];
+      sB[0] = s[1];
+      qk_block<D>(Ks, qf, 1, c, hh, s);
+      sA[1] = s[0];
+      sB[1] = s[1];
     }
     if (k0 + kBN > w.len) {  // last, partial tile
 #pragma unroll
@@ -178,69 +262,54 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key >= w.len) s[kb][r] = -INFINITY;
+          if (key >= w.len) {
+            sA[kb][r] = -INFINITY;
+            sB[kb][r] = -INFINITY;
+          }
         }
     }
+    bf16x8 pA[4], pB[4];
+    softmax_block<DBLK>(sA[0], sA[1], rs[0], o[0], scale_log2, pA);
+    softmax_block<DBLK>(sB[0], sB[1], rs[1], o[1], scale_log2, pB);
 
-    // ---- online softmax (log2 domain)
-    float mx = -INFINITY;
+    // O^T += V^T P^T: operand k = 2*kb + t covers keys kb*32 + 16t .. +15
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int k = 0; k < 4; ++k) {
+      const int r1 = (k >> 1) * 32 + 16 * (k & 1) + 4 * hh + tr_r;
+      const int r2 = r1 + 8;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * scale_log2);
-    const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale_log2, -m_new));
-        s[kb][r] = p;
-        rs += p;
+      for (int db = 0; db < DBLK; ++db) {
+        const int col = 32 * db + 16 * tr_g + 4 * tr_q;
+        const int ch = col >> 3, within = col & 7;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(Vs + r1 * D + ((ch ^ vswz(r1, CPR)) << 3) + within));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(Vs + r2 * D + ((ch ^ vswz(r2, CPR)) << 3) + within));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pA[k], o[0][db], 0, 0, 0);
+        o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pB[k], o[1][db], 0, 0, 0);
       }
-    l_run = l_run * corr + rs;
-#pragma unroll
-    for (int db = 0; db < DBLK; ++db) o[db] *= corr;
+    }
+  };
 
-    // ---- O^T += V^T P^T, 16 keys per MFMA
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        bf16x8 pb;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pb[j] = (__bf16)s[kb][8 * t + j];
-        const int r1 = kb * 32 + 16 * t + 4 * hh + tr_r;
-        const int r2 = r1 + 8;
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db) {
-          const int col = 32 * db + 16 * tr_g + 4 * tr_q;
-          const int ch = col >> 3, within = col & 7;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(Vs + r1 * D + ((ch ^ vswz(r1, CPR)) << 3) + within));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(Vs + r2 * D + ((ch ^ vswz(r2, CPR)) << 3) + within));
-          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[db], 0, 0, 0);
-        }
-      }
-    __syncthreads();  // the next tile overwrites Ks / Vs
+  for (int t = 0; t < ntiles; t += 2) {
+    tile(Ks0, Vs0, Ks1, Vs1, t);
+    if (t + 1 < ntiles) tile(Ks1, Vs1, Ks0, Vs0, t + 1);
   }
 
   // ---- normalise and store: reg r of block db is channel 32*db + 8*(r/4) + 4*hh + r%4
-  const float inv = 1.0f / (l_run + __shfl_xor(l_run, 32));
-  if (qvalid) {
-    uint16_t* op = O + qrow * row_stride + hoff;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const float inv = 1.0f / (rs[b].l + __shfl_xor(rs[b].l, 32));
+    if (!qvalid[b]) continue;
+    uint16_t* op = O + qrow[b] * row_stride + hoff;
 #pragma unroll
     for (int db = 0; db < DBLK; ++db)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int d0 = 32 * db + 8 * b + 4 * hh;
-        float v0 = o[db][4 * b] * inv, v1 = o[db][4 * b + 1] * inv;
-        float v2 = o[db][4 * b + 2] * inv, v3 = o[db][4 * b + 3] * inv;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = 32 * db + 8 * q4 + 4 * hh;
+        float v0 = o[b][db][4 * q4] * inv, v1 = o[b][db][4 * q4 + 1] * inv;
+        float v2 = o[b][db][4 * q4 + 2] * inv, v3 = o[b][db][4 * q4 + 3] * inv;
         if constexpr (kStga) {
           v0 *= alpha; v1 *= alpha; v2 *= alpha; v3 *= alpha;
           if (beta != 0.f) {
