@@ -8,29 +8,43 @@
 // section.  The online (running max / running sum) softmax is the one of the
 // FlashAttention papers the pages cite; the tiling here is our own for CDNA4.
 //
-// Work item = (group, head, tile of 128 queries); a workgroup of 4 waves owns
-// one item, each wave 32 queries.  Per 64-key tile:
-//   K and V rows are staged in LDS (16-byte XOR-swizzled chunks, conflict-free
-//   writes and reads);
+// Work item = (group, head, tile of 256 queries), one workgroup each.  A wave
+// owns QB blocks of 32 queries (QB = 1: 8 waves, two per SIMD, so the
+// hardware interleaves one wave's softmax with the other's MFMAs; QB = 2:
+// 4 waves, one per SIMD, each K/V operand read feeding two MFMAs).  Per
+// 64-key tile:
+//   K and V rows arrive in LDS by 16-byte direct-to-LDS loads, double
+//   buffered (the next tile streams in while this one computes) and
+//   XOR-swizzled at 16-byte granularity (conflict-free reads);
 //   S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = the
 //   wave's Q fragment held in registers) -- the C layout gives every lane one
-//   query and 16 keys, so the softmax statistics stay in-lane (the two wave
-//   halves share a query and exchange one value);
-//   online softmax in float32 with exp2 and the scale folded into one FMA;
+//   query and 16 keys, so softmax statistics stay in-lane (the two wave
+//   halves share a query and exchange one value with v_permlane32_swap);
+//   softmax in float32 with exp2 and the scale folded into one FMA, against
+//   an exponent offset fixed from each row's first 32 keys (no accumulator
+//   rescaling; a work item whose later scores exceed that offset by 2^32 is
+//   recomputed with exact row maxima);
 //   O^T += V^T P^T with the same MFMA: B = P^T comes straight from the S^T
 //   registers (the k-slot order of an MFMA is free as long as both operands
 //   agree), A = V^T comes from row-major V in LDS through ds_read_b64_tr_b16.
 // Items are handed out largest group first (longest-processing-time order) and
 // dealt to the 8 XCDs in runs of consecutive query tiles of one (group, head),
 // so tiles that stream the same K/V run side by side under one L2.
+#include <type_traits>
+
+#ifndef MOGA_ATTN_QB
+#define MOGA_ATTN_QB 1
+#endif
+
 #include "moga_internal.h"
 
 namespace moga {
 namespace {
 
-constexpr int kAttnWaves = 4;
-constexpr int kQueriesPerWave = 64;
-constexpr int kBM = kAttnWaves * kQueriesPerWave;  // queries per workgroup
+constexpr int kBM = 256;  // queries per workgroup (work item)
+constexpr int kQB = MOGA_ATTN_QB;                   // 32-query blocks per wave (1 or 2)
+template <int QB>
+constexpr int waves_for() { return kBM / (32 * QB); }
 constexpr int kBN = 64;                             // keys per LDS tile
 constexpr int kXcdRun = 8;                          // consecutive items per XCD
 
@@ -106,23 +120,37 @@ typedef __attribute__((address_space(1))) void global_void;
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Softmax bookkeeping of one 32-query block (one query per lane; the two wave
-// halves hold the same query and exchange one value).
+// halves hold the same query).  The exponent offset m_ref is fixed from the
+// row's first 32 keys and never moves, so the output accumulator is never
+// rescaled; a later score more than 2^kTau above it raises `over`, and the
+// work item is then recomputed with the exact row max (see attn_kernel).
 struct RowState {
-  float m_used;  // exponent offset in use (log2 domain)
-  float l;       // this lane's share of the denominator
+  float m_ref;  // exponent offset (log2 domain); -inf until the first keys
+  float l;      // this lane's share of the denominator
 };
+constexpr float kTau = 32.0f;
+
+// max / sum of a value over the two wave halves (lanes c and c+32 share a query)
+__device__ __forceinline__ float halves_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Issue one K/V tile (kBN rows starting at group-local key k0) into LDS with
 // 16-byte direct-to-LDS loads.  Lane i of a load lands at LDS base + 16*i, so
 // the swizzle is applied on the source side: the lane writing physical chunk p
 // of row r fetches logical chunk p ^ swz(r).  Rows past the group end repeat
 // the last row (finite data; their scores are masked).
-template <int D, class Rows>
+template <int D, int NW, class Rows>
 __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                                            uint16_t* Ks, uint16_t* Vs, const Rows& rows, const Work& w,
                                            int64_t row_stride, int64_t hoff, int k0, int wave, int lane) {
   constexpr int CPR = D / 8;
-  constexpr int LOADS = kBN * CPR / (kAttnWaves * kWave);  // per wave, per tensor
+  constexpr int LOADS = kBN * CPR / (NW * kWave);  // per wave, per tensor
 #pragma unroll
   for (int j = 0; j < LOADS; ++j) {
     const int q = (wave * LOADS + j) * kWave + lane;  // chunk index inside the tile
@@ -138,71 +166,131 @@ __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ K, const
   }
 }
 
-// S^T for one 32-key block kb of the tile and both query blocks of the wave:
-// reg r of s[b] is key kb*32 + 8*(r/4) + 4*hh + r%4, query c of block b.
-template <int D>
-__device__ __forceinline__ void qk_block(const uint16_t* Ks, const bf16x8 (&qf)[2][D / 16], int kb, int c, int hh,
-                                         f32x16 (&s)[2]) {
-  constexpr int CPR = D / 8;
-  s[0] = f32x16{};
-  s[1] = f32x16{};
-  const int krow = kb * 32 + c;
+// Softmax step of one query block over one 32-key half of a tile: bf16 P^T
+// operands of the half's two 16-key MFMA steps go to pb, their sum to st.l.
+// s: reg r is key 8*(r/4) + 4*hh + r%4 of the half (masked keys are -inf).
+__device__ __forceinline__ void softmax_half(const f32x16& s, RowState& st, float scale_log2, bf16x8 (&pb)[2],
+                                             bool& over) {
+  float mx = s[0];
 #pragma unroll
-  for (int st = 0; st < D / 16; ++st) {
-    const int ch = 2 * st + hh;
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + krow * D + (ch ^ kswz(krow, CPR)) * 8);
-    s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][st], s[0], 0, 0, 0);
-    s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[1][st], s[1], 0, 0, 0);
-  }
-}
-
-// Online softmax of one query block over the 64 keys of a tile (s0: keys
-// 0-31, s1: keys 32-63), turning the scores into bf16 P^T operands.  The
-// accumulator is rescaled only when the row max grows by more than 2^kTau.
-constexpr float kTau = 8.0f;
-template <int DBLK>
-__device__ __forceinline__ void softmax_block(f32x16& s0, f32x16& s1, RowState& st, f32x16 (&o)[DBLK],
-                                              float scale_log2, bf16x8 (&pb)[4]) {
-  float mx = -INFINITY;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = mx * scale_log2;
-  const bool need = m_new > st.m_used + kTau;
-  if (__builtin_amdgcn_read_exec() & __ballot(need)) {  // wave-uniform
-    const float target = need ? m_new : st.m_used;
-    const float corr = __builtin_amdgcn_exp2f(st.m_used - target);
-    st.m_used = target;
-    st.l *= corr;
-#pragma unroll
-    for (int db = 0; db < DBLK; ++db) o[db] *= corr;
-  }
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+  const float m_new = halves_max(mx) * scale_log2;
+  st.m_ref = st.m_ref == -INFINITY ? m_new : st.m_ref;
+  over |= m_new > st.m_ref + kTau;
   float rs = 0.f;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const float p0 = __builtin_amdgcn_exp2f(fmaf(s0[r], scale_log2, -st.m_used));
-    const float p1 = __builtin_amdgcn_exp2f(fmaf(s1[r], scale_log2, -st.m_used));
-    s0[r] = p0;
-    s1[r] = p1;
-    rs += p0 + p1;
-  }
-  st.l += rs;
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      pb[t][j] = (__bf16)s0[8 * t + j];
-      pb[2 + t][j] = (__bf16)s1[8 * t + j];
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[8 * t + j], scale_log2, -st.m_ref));
+      pb[t][j] = (__bf16)p;
+      rs += p;
     }
+  st.l += rs;
 }
 
-template <int D, class Rows, bool kStga>
-__global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(
+// S^T of one 32-key half kb for the wave's QB query blocks; each K operand
+// read from LDS feeds QB MFMAs.  Reg r of s[b] is key kb*32 + 8*(r/4) + 4*hh + r%4.
+template <int D, int QB>
+__device__ __forceinline__ void qk_half(const uint16_t* Ks, const bf16x8 (&qf)[QB][D / 16], int kb, int lane,
+                                        f32x16 (&s)[QB]) {
+  constexpr int CPR = D / 8;
+  const int hh = lane >> 5, krow = kb * 32 + (lane & 31);
+#pragma unroll
+  for (int b = 0; b < QB; ++b) s[b] = f32x16{};
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + krow * D + ((2 * st + hh) ^ kswz(krow, CPR)) * 8);
+#pragma unroll
+    for (int b = 0; b < QB; ++b) s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[b][st], s[b], 0, 0, 0);
+  }
+}
+
+// O^T += V^T P^T for one 32-key half kb and the wave's query blocks; each V^T
+// operand (two transposing LDS reads) feeds QB MFMAs.
+template <int D, int QB>
+__device__ __forceinline__ void pv_half(const uint16_t* Vs, const bf16x8 (&p)[QB][2], int kb, int lane,
+                                        f32x16 (&o)[QB][D / 32]) {
+  constexpr int CPR = D / 8;
+  const int hh = lane >> 5;
+  const int tr_r = (lane & 15) >> 2, tr_q = lane & 3, tr_g = (lane >> 4) & 1;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int r1 = kb * 32 + 16 * t + 4 * hh + tr_r;
+    const int r2 = r1 + 8;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int col = 32 * db + 16 * tr_g + 4 * tr_q;
+      const int ch = col >> 3, within = col & 7;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(Vs + r1 * D + ((ch ^ vswz(r1, CPR)) << 3) + within));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(Vs + r2 * D + ((ch ^ vswz(r2, CPR)) << 3) + within));
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int b = 0; b < QB; ++b) o[b][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[b][t], o[b][db], 0, 0, 0);
+    }
+  }
+}
+
+template <bool kMask, int QB>
+__device__ __forceinline__ void mask_half(f32x16 (&s)[QB], int key0, int len, int hh) {
+  if constexpr (kMask) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if (key0 + 8 * (r >> 2) + 4 * hh + (r & 3) >= len) {
+#pragma unroll
+        for (int b = 0; b < QB; ++b) s[b][r] = -INFINITY;
+      }
+    }
+  }
+}
+
+// One 64-key tile for the wave's query blocks, in 32-key halves:
+//   QK(h0) QK(h1) | softmax(h0) PV(h0) | softmax(h1) PV(h1)
+template <int D, int QB, bool kMask>
+__device__ __forceinline__ void tile_step(const uint16_t* Ks, const uint16_t* Vs, int k0, int len,
+                                          const bf16x8 (&qf)[QB][D / 16], f32x16 (&o)[QB][D / 32],
+                                          RowState (&rs)[QB], float scale_log2, int lane, bool& over) {
+  const int hh = lane >> 5;
+  f32x16 s0[QB], s1[QB];
+  bf16x8 p[QB][2];
+  qk_half<D, QB>(Ks, qf, 0, lane, s0);
+  qk_half<D, QB>(Ks, qf, 1, lane, s1);
+  mask_half<kMask, QB>(s0, k0, len, hh);
+#pragma unroll
+  for (int b = 0; b < QB; ++b) softmax_half(s0[b], rs[b], scale_log2, p[b], over);
+  pv_half<D, QB>(Vs, p, 0, lane, o);
+  mask_half<kMask, QB>(s1, k0 + 32, len, hh);
+#pragma unroll
+  for (int b = 0; b < QB; ++b) softmax_half(s1[b], rs[b], scale_log2, p[b], over);
+  pv_half<D, QB>(Vs, p, 1, lane, o);
+}
+
+// Row maxima only (the first pass of the exact recomputation).
+template <int D, int QB, bool kMask>
+__device__ __forceinline__ void tile_max(const uint16_t* Ks, int k0, int len, const bf16x8 (&qf)[QB][D / 16],
+                                         float (&mx)[QB], int lane) {
+  const int hh = lane >> 5;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    f32x16 s[QB];
+    qk_half<D, QB>(Ks, qf, kb, lane, s);
+    mask_half<kMask, QB>(s, k0 + 32 * kb, len, hh);
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx[b] = fmaxf(mx[b], s[b][r]);
+  }
+}
+
+template <int D, int QB, class Rows, bool kStga>
+__global__ __launch_bounds__(waves_for<QB>() * kWave) void attn_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, int64_t row_stride, float scale_log2, float alpha, float beta, Rows rows) {
-  constexpr int CPR = D / 8;
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
+  constexpr int NW = waves_for<QB>();
   __shared__ __attribute__((aligned(1024))) uint16_t Ks0[kBN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t Vs0[kBN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t Ks1[kBN * D];
@@ -214,17 +302,18 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, c = lane & 31;
   const int64_t hoff = (int64_t)w.head * D;
+  const int nfull = w.len / kBN;            // tiles without a group end inside
   const int ntiles = (w.len + kBN - 1) / kBN;
 
-  issue_tile<D>(K, V, Ks0, Vs0, rows, w, row_stride, hoff, 0, wave, lane);
+  issue_tile<D, NW>(K, V, Ks0, Vs0, rows, w, row_stride, hoff, 0, wave, lane);
 
   // this lane's two queries (blocks b = 0, 1) and their Q fragments
-  int64_t qrow[2];
-  bool qvalid[2];
-  bf16x8 qf[2][KSTEPS];
+  int64_t qrow[QB];
+  bool qvalid[QB];
+  bf16x8 qf[QB][KSTEPS];
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int qi = w.q0 + wave * kQueriesPerWave + b * 32 + c;
+  for (int b = 0; b < QB; ++b) {
+    const int qi = w.q0 + (wave * QB + b) * 32 + c;
     qvalid[b] = qi < w.len;
     qrow[b] = rows.row(w, qvalid[b] ? qi : w.len - 1);
     const uint16_t* qp = Q + qrow[b] * row_stride + hoff + 8 * hh;
@@ -232,75 +321,84 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(
     for (int s = 0; s < KSTEPS; ++s) qf[b][s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
   }
 
-  f32x16 o[2][DBLK];
+  f32x16 o[QB][DBLK];
+  RowState rs[QB];
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+  for (int b = 0; b < QB; ++b) {
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) o[b][db] = f32x16{};
-  RowState rs[2] = {{-INFINITY, 0.f}, {-INFINITY, 0.f}};
-  const int tr_r = (lane & 15) >> 2, tr_q = lane & 3, tr_g = (lane >> 4) & 1;
+    rs[b] = {-INFINITY, 0.f};
+  }
+  bool over = false;
 
-  auto tile = [&](const uint16_t* Ks, const uint16_t* Vs, uint16_t* Kn, uint16_t* Vn, int t) {
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile t have landed
-    __syncthreads();                // ... and every wave's; tile t-1 is fully consumed
-    if (t + 1 < ntiles) issue_tile<D>(K, V, Kn, Vn, rows, w, row_stride, hoff, (t + 1) * kBN, wave, lane);
-    const int k0 = t * kBN;
-
-    f32x16 sA[2], sB[2];  // [query block][32-key block]
-    {
-      f32x16 s[2];
-      qk_block<D>(Ks, qf, 0, c, hh, s);
-      sA[0] = s[0];
-      sB[0] = s[1];
-      qk_block<D>(Ks, qf, 1, c, hh, s);
-      sA[1] = s[0];
-      sB[1] = s[1];
+  // Tile t lives in buffer t % 2.  At the top of each tile: wait for this
+  // wave's loads, barrier (all waves' loads landed, tile t-1 fully consumed),
+  // then start the loads of tile t+1 into the other buffer.
+  auto begin_tile = [&](uint16_t* Kn, uint16_t* Vn, int t) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t + 1 < ntiles) issue_tile<D, NW>(K, V, Kn, Vn, rows, w, row_stride, hoff, (t + 1) * kBN, wave, lane);
+  };
+  // kMax: row maxima only (into mx) instead of softmax and P V
+  auto run = [&](auto max_only) {
+    constexpr bool kMax = decltype(max_only)::value;
+    float mx[QB];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) mx[b] = -INFINITY;
+    auto step = [&](const uint16_t* Ks, const uint16_t* Vs, int t, auto mask) {
+      constexpr bool kMask = decltype(mask)::value;
+      if constexpr (kMax)
+        tile_max<D, QB, kMask>(Ks, t * kBN, w.len, qf, mx, lane);
+      else
+        tile_step<D, QB, kMask>(Ks, Vs, t * kBN, w.len, qf, o, rs, scale_log2, lane, over);
+    };
+    using F = std::false_type;
+    using T = std::true_type;
+    int t = 0;
+    for (; t + 2 <= nfull; t += 2) {
+      begin_tile(Ks1, Vs1, t);
+      step(Ks0, Vs0, t, F{});
+      begin_tile(Ks0, Vs0, t + 1);
+      step(Ks1, Vs1, t + 1, F{});
     }
-    if (k0 + kBN > w.len) {  // last, partial tile
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key >= w.len) {
-            sA[kb][r] = -INFINITY;
-            sB[kb][r] = -INFINITY;
-          }
-        }
-    }
-    bf16x8 pA[4], pB[4];
-    softmax_block<DBLK>(sA[0], sA[1], rs[0], o[0], scale_log2, pA);
-    softmax_block<DBLK>(sB[0], sB[1], rs[1], o[1], scale_log2, pB);
-
-    // O^T += V^T P^T: operand k = 2*kb + t covers keys kb*32 + 16t .. +15
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int r1 = (k >> 1) * 32 + 16 * (k & 1) + 4 * hh + tr_r;
-      const int r2 = r1 + 8;
-#pragma unroll
-      for (int db = 0; db < DBLK; ++db) {
-        const int col = 32 * db + 16 * tr_g + 4 * tr_q;
-        const int ch = col >> 3, within = col & 7;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(Vs + r1 * D + ((ch ^ vswz(r1, CPR)) << 3) + within));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(Vs + r2 * D + ((ch ^ vswz(r2, CPR)) << 3) + within));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pA[k], o[0][db], 0, 0, 0);
-        o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pB[k], o[1][db], 0, 0, 0);
+    if (t < ntiles) {  // one or two tiles left, the last may be partial; t is even
+      begin_tile(Ks1, Vs1, t);
+      if (t < nfull)
+        step(Ks0, Vs0, t, F{});
+      else
+        step(Ks0, Vs0, t, T{});
+      if (t + 1 < ntiles) {
+        begin_tile(Ks0, Vs0, t + 1);
+        step(Ks1, Vs1, t + 1, T{});
       }
     }
+    if constexpr (kMax) {
+#pragma unroll
+      for (int b = 0; b < QB; ++b) rs[b] = {halves_max(mx[b]) * scale_log2, 0.f};
+    }
   };
+  run(std::false_type{});
 
-  for (int t = 0; t < ntiles; t += 2) {
-    tile(Ks0, Vs0, Ks1, Vs1, t);
-    if (t + 1 < ntiles) tile(Ks1, Vs1, Ks0, Vs0, t + 1);
+  // A score far above a row's first keys would overflow the fixed offset:
+  // recompute this work item exactly (row maxima first, then softmax and P V
+  // with the exact maxima, where no score exceeds its offset).
+  if (__syncthreads_or(over)) {
+    __syncthreads();
+    issue_tile<D, NW>(K, V, Ks0, Vs0, rows, w, row_stride, hoff, 0, wave, lane);
+    run(std::true_type{});
+    __syncthreads();
+    issue_tile<D, NW>(K, V, Ks0, Vs0, rows, w, row_stride, hoff, 0, wave, lane);
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) o[b][db] = f32x16{};
+    run(std::false_type{});
   }
 
   // ---- normalise and store: reg r of block db is channel 32*db + 8*(r/4) + 4*hh + r%4
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const float inv = 1.0f / (rs[b].l + __shfl_xor(rs[b].l, 32));
+  for (int b = 0; b < QB; ++b) {
+    const float inv = 1.0f / halves_sum(rs[b].l);
     if (!qvalid[b]) continue;
     uint16_t* op = O + qrow[b] * row_stride + hoff;
 #pragma unroll
@@ -362,7 +460,7 @@ int launch_attn(const void* Q, const void* K, const void* V, void* O, int64_t ro
   const int64_t run = (int64_t)kNumXcd * kXcdRun;
   const int64_t grid = ceil_div(items_bound, run) * run;
   if (grid > 0x7fffffff) return MOGA_ERR_SHAPE;
-  attn_kernel<D, Rows, kStga><<<dim3((unsigned)grid), kAttnWaves * kWave, 0, st>>>(
+  attn_kernel<D, kQB, Rows, kStga><<<dim3((unsigned)grid), waves_for<kQB>() * kWave, 0, st>>>(
       static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V),
       static_cast<uint16_t*>(O), row_stride, scale * 1.4426950408889634f, alpha, beta, rows);
   MOGA_LAUNCH_CHECK();

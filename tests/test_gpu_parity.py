@@ -167,3 +167,24 @@ def test_full_size_sampled(moga, name):
     got = _np(O[torch.from_numpy(rows).to(DEV)])
     e = assert_output_close(got, want, f"{name} sampled O")
     print(f"[parity] full {name}: {rows.size} rows, {e}", flush=True)
+
+
+@pytest.mark.parametrize("late,label", [(2.0, "overflow-fallback"), (0.9, "fixed-offset")])
+def test_attention_score_growth(moga, late, label):
+    """Scores that grow far beyond a row's first keys: with late = 2, q.k jumps
+    from 0 to ~512 (about 65 in log2 units after scaling) and the exact
+    recomputation path must engage; with late = 0.9 the growth stays inside
+    the fixed-offset range (2^32) and the main path handles it."""
+    print(f"[parity] score growth {label}", flush=True)
+    N, H, D = 700, 2, 128
+    g = torch.Generator().manual_seed(7)
+    Q = torch.full((N, H, D), 2.0).bfloat16()
+    K = torch.zeros((N, H, D))
+    K[200:] = late + 0.25 * torch.randn((N - 200, H, D), generator=g)
+    K = K.bfloat16()
+    V = torch.randn((N, H, D), generator=g).bfloat16()
+    cu = torch.tensor([0, 100, N], dtype=torch.int32)    # second group starts with zero keys
+    Op = moga.moga_group_attention(Q.to(DEV), K.to(DEV), V.to(DEV), cu.to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.group_attention(_np(Q), _np(K), _np(V), cu.numpy(), 1 / math.sqrt(D))
+    assert_output_close(_np(Op), ref, f"Op ({label})")
