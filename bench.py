@@ -39,8 +39,23 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=800, help="sampled query rows per group for the oracle")
+    ap.add_argument("--cpu-rows", type=int, default=2000, help="sampled query rows per group for the oracle")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run plain device copies of MIB MiB (reference for HBM byte counters)")
     return ap.parse_args()
+
+
+def calibrate_copy(mib):
+    """Plain device-to-device copies of a known size: the reference the
+    FETCH_SIZE / WRITE_SIZE counters are scaled by."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").random_(0, 255)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}), flush=True)
 
 
 def attn_flops(counts, H, D):
@@ -110,6 +125,10 @@ def main():
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not supported. "
               "Multi-GPU sharding is described in DESIGN.md, not implemented.", file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     import torch
 
