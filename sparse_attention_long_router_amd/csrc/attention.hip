@@ -198,11 +198,18 @@ __device__ __forceinline__ void qk_half(const uint16_t* Ks, const bf16x8 (&qf)[Q
   const int hh = lane >> 5, krow = kb * 32 + (lane & 31);
 #pragma unroll
   for (int b = 0; b < QB; ++b) s[b] = f32x16{};
+  // All K operands of the half first, then the dependent MFMA chain: without
+  // the fence the scheduler reuses one operand register and exposes an LDS
+  // round trip before every MFMA of the chain.
+  bf16x8 ka[D / 16];
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st)
+    ka[st] = *reinterpret_cast<const bf16x8*>(Ks + krow * D + ((2 * st + hh) ^ kswz(krow, CPR)) * 8);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int st = 0; st < D / 16; ++st) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + krow * D + ((2 * st + hh) ^ kswz(krow, CPR)) * 8);
 #pragma unroll
-    for (int b = 0; b < QB; ++b) s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[b][st], s[b], 0, 0, 0);
+    for (int b = 0; b < QB; ++b) s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st], qf[b][st], s[b], 0, 0, 0);
   }
 }
 
