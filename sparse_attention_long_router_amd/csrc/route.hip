@@ -13,10 +13,10 @@
 //   A = W_r fragment (16 groups x 32 k), B = X^T fragment (32 k x 16 tokens),
 //   lane (q = lane/16, c = lane%16) feeds A row c / B column c with the 8
 //   k-values of slot q; C reg r holds group 4q+r of token c.
-// The k-slots of one MFMA need not be consecutive channels as long as A and B
-// agree, so in the main loop each lane reads 64 contiguous bytes of its token
-// row (channels q*32 .. q*32+31 of a 128-channel step) and feeds them to four
-// MFMAs -- 16-byte loads, whole cache lines used.
+// Per 128-channel step each lane issues four 16-byte loads: load j covers
+// channels j*32 + q*8 .. +7 of its token, so one load instruction reads 64
+// contiguous bytes of each of 16 token rows (the four lane quads take adjacent
+// chunks) and the four loads together cover 256 contiguous bytes per row.
 #include "moga_internal.h"
 
 namespace moga {
@@ -55,27 +55,41 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void route_kernel(
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[tb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  int k0 = 0;
-  // main loop: 128 channels per step, 64 contiguous bytes per lane and row
-  for (; k0 + 128 <= dm; k0 += 128) {
-    const int kq = k0 + q * 32;
-    bf16x8 xf[kRouteTokBlocks][4], wf[MB][4];
+  // main loop: 128 channels per step, software-pipelined so the loads of step
+  // k+1 are in flight while step k's MFMAs run
+  const int nmain = dm / 128;
+  bf16x8 xf[2][kRouteTokBlocks][4], wf[2][MB][4];
+  auto load_step = [&](int buf, int kbase) {
+    const int kq = kbase + q * 8;
 #pragma unroll
     for (int tb = 0; tb < kRouteTokBlocks; ++tb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) xf[tb][j] = *reinterpret_cast<const bf16x8*>(xrow[tb] + kq + j * 8);
+      for (int j = 0; j < 4; ++j)
+        xf[buf][tb][j] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(xrow[tb] + kq + j * 32));
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) wf[mb][j] = *reinterpret_cast<const bf16x8*>(wrow[mb] + kq + j * 8);
+      for (int j = 0; j < 4; ++j) wf[buf][mb][j] = *reinterpret_cast<const bf16x8*>(wrow[mb] + kq + j * 32);
+  };
+  auto mfma_step = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int tb = 0; tb < kRouteTokBlocks; ++tb)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
-          acc[tb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[mb][j], xf[tb][j], acc[tb][mb], 0, 0, 0);
+          acc[tb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[buf][mb][j], xf[buf][tb][j], acc[tb][mb], 0, 0, 0);
+  };
+  if (nmain > 0) load_step(0, 0);
+  int i = 0;
+  for (; i + 2 <= nmain; i += 2) {
+    load_step(1, (i + 1) * 128);
+    mfma_step(0);
+    if (i + 2 < nmain) load_step(0, (i + 2) * 128);
+    mfma_step(1);
   }
+  if (i < nmain) mfma_step(0);
+  int k0 = nmain * 128;
   // tail: 32 channels per step (d_model is a multiple of 32)
   for (; k0 < dm; k0 += 32) {
     const int kq = k0 + q * 8;
