@@ -3,13 +3,15 @@
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 A step is one pass of the whole path over one synthetic batch already resident
-in HBM: route -> permute (sort + Q/K/V gather) -> group attention -> gated
-unpermute (-> STGA sum for workloads that have it).  Prints ONE JSON line.
+in HBM: route -> permute (sort + Q/K/V gather) -> group attention with the
+gated unpermute fused in (-> STGA sum for workloads that have it).  Prints ONE
+JSON line.
 
 value = effective TFLOP/s of the whole step, counting only within-group
 attention FLOPs 4*H*D*sum_g n_g^2 (plus the STGA windows when present);
 tokens_per_s = N / step time.  The roofline object covers the dominant kernel
-(group attention), timed live with HIP events on the stream it runs on.
+(group attention with the gated unpermute fused in), timed live with HIP
+events on the stream it runs on.
 """
 
 from __future__ import annotations
@@ -145,7 +147,8 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
-        # same five library calls as MogaForward.__call__, with events between stages
+        # the library calls of MogaForward.__call__ (fused attention + unpermute),
+        # with HIP events on the same stream between stages
         if ev is not None:
             ev[0].record(stream)
         moga.moga_route(X, Wr, None, fwd.group_id, fwd.gate)
@@ -155,24 +158,22 @@ def main():
                           fwd.max_seqlen, fwd.ws_perm)
         if ev is not None:
             ev[2].record(stream)
-        moga.moga_group_attention(fwd.Qp, fwd.Kp, fwd.Vp, fwd.cu_seqlens, 0.0, fwd.Op, fwd.ws_attn)
+        moga.moga_group_attention_unpermute(fwd.Qp, fwd.Kp, fwd.Vp, fwd.cu_seqlens, fwd.perm, fwd.gate, 0.0, 0.0,
+                                            fwd.O, fwd.ws_attn)
         if ev is not None:
             ev[3].record(stream)
-        moga.moga_unpermute(fwd.Op, fwd.perm, fwd.gate, 0.0, fwd.O)
-        if ev is not None:
-            ev[4].record(stream)
         if wl.stga is not None:
             s = wl.stga
             moga.moga_stga_attention(Q, K, V, s["T"], s["Hs"], s["Ws"], s["win_t"], s["tile_h"], s["tile_w"],
                                      0.0, 1.0, 1.0, fwd.O)
         if ev is not None:
-            ev[5].record(stream)
+            ev[4].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -181,7 +182,7 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
-    stages = ["route", "permute", "group_attention", "unpermute", "stga"]
+    stages = ["route", "permute", "group_attention_unpermute", "stga"]
     breakdown = {s: sum(e[k].elapsed_time(e[k + 1]) for e in evs) / args.steps for k, s in enumerate(stages)}
     if wl.stga is None:
         breakdown.pop("stga")
@@ -195,13 +196,13 @@ def main():
         flops_stga = 4.0 * wl.H * wl.D * gsize * gsize * (wl.N // gsize)
     step_flops = flops_moga + flops_stga
     value = step_flops / (ms_per_step * 1e-3) / 1e12
-    attn_ms = breakdown["group_attention"]
+    attn_ms = breakdown["group_attention_unpermute"]
     achieved = flops_moga / (attn_ms * 1e-3) / 1e12
 
     traffic = traffic_entry(None)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "kernel": "attn_kernel (moga_group_attention)", "launch_ms": round(attn_ms, 4),
+                "kernel": "attn_kernel (moga_group_attention_unpermute)", "launch_ms": round(attn_ms, 4),
                 "flops_per_launch": flops_moga}
     mean = wl.N / wl.M
     out = {
@@ -230,7 +231,6 @@ def main():
     hbm = {  # algorithmic bytes per launch of the HBM-bound stages
         "route": wl.N * (2 * wl.d_model + 8) + 2 * wl.M * wl.d_model,
         "permute": wl.N * (12 * wl.H * wl.D + 16),
-        "unpermute": wl.N * (4 * wl.H * wl.D + 12),
     }
     out["hbm_gbs"] = {k: round(b / (breakdown[k] * 1e-3) / 1e9, 1) for k, b in hbm.items()}
     out["hbm_frac"] = {k: round(v / PEAK_HBM_GBS, 4) for k, v in out["hbm_gbs"].items()}

@@ -111,6 +111,19 @@ int moga_group_attention(const void* Qp, const void* Kp, const void* Vp,
                          void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moga_group_attention_unpermute -- moga_group_attention and moga_unpermute
+ *   in one kernel (MoGA output equation; Algorithm 1 steps 3 and 4): the
+ *   attention of permuted row j is written straight to its original token,
+ *   O[perm[j]] = beta * O[perm[j]] + gate[perm[j]] * Attn(j), without the
+ *   intermediate O_hat.  Arguments as in the two calls it replaces; ws as for
+ *   MOGA_OP_GROUP_ATTENTION.  beta = 0 does not read O.
+ */
+int moga_group_attention_unpermute(const void* Qp, const void* Kp, const void* Vp,
+                                   const int32_t* cu_seqlens, const int32_t* perm, const float* gate,
+                                   int64_t N, int32_t H, int32_t D, int32_t M, float softmax_scale,
+                                   float beta, void* O, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * moga_unpermute -- gate and return rows to original order
  *   (MoGA output equation in "Grouped Attention"; Algorithm 1 step 4):
  *   O[perm[j]] = beta * O[perm[j]] + gate[perm[j]] * Op[j]  (float32 math).

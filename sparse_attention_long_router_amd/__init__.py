@@ -2,10 +2,10 @@
 
 The computation lives in libmoga.so (hand-written HIP kernels behind the C ABI
 of include/moga.h); this package is its Python binding.  Importing it fails if
-the library has not been built (`python -m sparse_attention_long_router_amd.build`).
+the library has not been built (`python sparse_attention_long_router_amd/build.py`).
 """
 
 from ._lib import (MOGA_OP_GROUP_ATTENTION, MOGA_OP_PERMUTE, MOGA_OP_ROUTE,  # noqa: F401
                    MOGA_OP_STGA_ATTENTION, MOGA_OP_UNPERMUTE, LIB_PATH, MogaError, version)
-from .binding import (MogaForward, moga_group_attention, moga_permute, moga_route,  # noqa: F401
-                      moga_stga_attention, moga_unpermute, moga_workspace_bytes)
+from .binding import (MogaForward, moga_group_attention, moga_group_attention_unpermute,  # noqa: F401
+                      moga_permute, moga_route, moga_stga_attention, moga_unpermute, moga_workspace_bytes)

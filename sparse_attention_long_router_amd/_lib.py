@@ -29,6 +29,8 @@ SIGNATURES = {
     "moga_permute": (_c.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _sz, _vp]),
     "moga_group_attention": (_c.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _f32, _vp, _vp, _sz, _vp]),
+    "moga_group_attention_unpermute": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _f32,
+                                                   _f32, _vp, _vp, _sz, _vp]),
     "moga_unpermute": (_c.c_int, [_vp, _vp, _vp, _i64, _i32, _i32, _f32, _vp, _vp]),
     "moga_stga_attention": (_c.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                                        _f32, _f32, _vp, _vp]),
@@ -38,12 +40,18 @@ SIGNATURES = {
 }
 
 
+BUILD_HINT = "run `python sparse_attention_long_router_amd/build.py`"
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m sparse_attention_long_router_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; {BUILD_HINT}")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
-        fn = getattr(lib, name)
+        try:
+            fn = getattr(lib, name)
+        except AttributeError:
+            raise ImportError(f"{LIB_PATH} lacks {name} (stale build); {BUILD_HINT}") from None
         fn.restype = res
         fn.argtypes = args
     return lib

@@ -111,6 +111,30 @@ def moga_group_attention(Qp, Kp, Vp, cu_seqlens, softmax_scale=0.0, Op=None, ws=
     return Op
 
 
+def moga_group_attention_unpermute(Qp, Kp, Vp, cu_seqlens, perm, gate, softmax_scale=0.0, beta=0.0, O=None,
+                                   ws=None):
+    """Group attention with the gated unpermute fused in: O[perm[j]] = beta*O + gate*Attn(j)."""
+    _need(Qp, "Qp", BF16, 3)
+    N, H, D = Qp.shape
+    _need(Kp, "Kp", BF16, 3, Qp.shape)
+    _need(Vp, "Vp", BF16, 3, Qp.shape)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _need(perm, "perm", torch.int32, 1, (N,))
+    _need(gate, "gate", torch.float32, 1, (N,))
+    M = cu_seqlens.shape[0] - 1
+    if O is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs an existing O")
+        O = torch.empty_like(Qp)
+    _need(O, "O", BF16, 3, Qp.shape)
+    ws, nbytes = _workspace(MOGA_OP_GROUP_ATTENTION, N, M, H, D, ws, Qp.device)
+    check(_lib.LIB.moga_group_attention_unpermute(ptr(Qp), ptr(Kp), ptr(Vp), ptr(cu_seqlens), ptr(perm), ptr(gate),
+                                                  N, H, D, M, float(softmax_scale), float(beta), ptr(O), ptr(ws),
+                                                  nbytes, stream_handle()),
+          "moga_group_attention_unpermute")
+    return O
+
+
 def moga_unpermute(Op, perm, gate, beta=0.0, O=None):
     """O[perm[j]] = beta * O[perm[j]] + gate[perm[j]] * Op[j]."""
     _need(Op, "Op", BF16, 3)
@@ -149,12 +173,14 @@ def moga_stga_attention(Q, K, V, T, Hs, Ws, win_t, tile_h, tile_w, softmax_scale
 
 class MogaForward:
     """Preallocated buffers for one MoGA layer pass (route, permute, group
-    attention, unpermute and, when ``stga`` geometry is given, the STGA sum).
-    ``__call__`` launches the five library calls back to back on the current
+    attention and gated unpermute -- fused into one kernel unless
+    ``fused=False`` -- and, when ``stga`` geometry is given, the STGA sum).
+    ``__call__`` launches the library calls back to back on the current
     stream and allocates nothing."""
 
-    def __init__(self, N, d_model, H, D, M, device, stga=None):
+    def __init__(self, N, d_model, H, D, M, device, stga=None, fused=True):
         self.N, self.d_model, self.H, self.D, self.M, self.stga = N, d_model, H, D, M, stga
+        self.fused = fused
         e = lambda *s, dt=BF16: torch.empty(*s, dtype=dt, device=device)  # noqa: E731
         self.group_id = e(N, dt=torch.int32)
         self.gate = e(N, dt=torch.float32)
@@ -170,8 +196,12 @@ class MogaForward:
         moga_route(X, Wr, bias, self.group_id, self.gate)
         moga_permute(self.group_id, self.M, Q, K, V, self.Qp, self.Kp, self.Vp, self.perm, self.cu_seqlens,
                      self.max_seqlen, self.ws_perm)
-        moga_group_attention(self.Qp, self.Kp, self.Vp, self.cu_seqlens, softmax_scale, self.Op, self.ws_attn)
-        moga_unpermute(self.Op, self.perm, self.gate, 0.0, self.O)
+        if self.fused:
+            moga_group_attention_unpermute(self.Qp, self.Kp, self.Vp, self.cu_seqlens, self.perm, self.gate,
+                                           softmax_scale, 0.0, self.O, self.ws_attn)
+        else:
+            moga_group_attention(self.Qp, self.Kp, self.Vp, self.cu_seqlens, softmax_scale, self.Op, self.ws_attn)
+            moga_unpermute(self.Op, self.perm, self.gate, 0.0, self.O)
         if self.stga is not None:
             g = self.stga
             moga_stga_attention(Q, K, V, g["T"], g["Hs"], g["Ws"], g["win_t"], g["tile_h"], g["tile_w"],

@@ -291,10 +291,22 @@ __device__ __forceinline__ void tile_max(const uint16_t* Ks, int k0, int len, co
   }
 }
 
-template <int D, int QB, class Rows, bool kStga>
+// Output stage of the attention kernel:
+//   kEpiPlain:  O[row] = attn                                  (permuted order)
+//   kEpiScaled: O[row] = alpha * attn + beta * O[row]          (STGA)
+//   kEpiGated:  n = perm[row]; O[n] = gate[n] * attn + beta * O[n]
+//               (the gated unpermute fused into the attention)
+enum { kEpiPlain = 0, kEpiScaled = 1, kEpiGated = 2 };
+struct Epilogue {
+  float alpha, beta;
+  const int32_t* perm;
+  const float* gate;
+};
+
+template <int D, int QB, class Rows, int kEpi>
 __global__ __launch_bounds__(waves_for<QB>() * kWave) void attn_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, int64_t row_stride, float scale_log2, float alpha, float beta, Rows rows) {
+    uint16_t* __restrict__ O, int64_t row_stride, float scale_log2, Epilogue epi, Rows rows) {
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
   constexpr int NW = waves_for<QB>();
@@ -407,21 +419,28 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave) void attn_kernel(
   for (int b = 0; b < QB; ++b) {
     const float inv = 1.0f / halves_sum(rs[b].l);
     if (!qvalid[b]) continue;
-    uint16_t* op = O + qrow[b] * row_stride + hoff;
+    float scale = inv, keep = 0.f;
+    int64_t orow = qrow[b];
+    if constexpr (kEpi == kEpiScaled) {
+      scale *= epi.alpha;
+      keep = epi.beta;
+    } else if constexpr (kEpi == kEpiGated) {
+      orow = epi.perm[qrow[b]];
+      scale *= epi.gate[orow];
+      keep = epi.beta;
+    }
+    uint16_t* op = O + orow * row_stride + hoff;
 #pragma unroll
     for (int db = 0; db < DBLK; ++db)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d0 = 32 * db + 8 * q4 + 4 * hh;
-        float v0 = o[b][db][4 * q4] * inv, v1 = o[b][db][4 * q4 + 1] * inv;
-        float v2 = o[b][db][4 * q4 + 2] * inv, v3 = o[b][db][4 * q4 + 3] * inv;
-        if constexpr (kStga) {
-          v0 *= alpha; v1 *= alpha; v2 *= alpha; v3 *= alpha;
-          if (beta != 0.f) {
-            const u32x2 old = *reinterpret_cast<const u32x2*>(op + d0);
-            v0 += beta * bf16_lo(old[0]); v1 += beta * bf16_hi(old[0]);
-            v2 += beta * bf16_lo(old[1]); v3 += beta * bf16_hi(old[1]);
-          }
+        float v0 = o[b][db][4 * q4] * scale, v1 = o[b][db][4 * q4 + 1] * scale;
+        float v2 = o[b][db][4 * q4 + 2] * scale, v3 = o[b][db][4 * q4 + 3] * scale;
+        if (kEpi != kEpiPlain && keep != 0.f) {
+          const u32x2 old = *reinterpret_cast<const u32x2*>(op + d0);
+          v0 += keep * bf16_lo(old[0]); v1 += keep * bf16_hi(old[0]);
+          v2 += keep * bf16_lo(old[1]); v3 += keep * bf16_hi(old[1]);
         }
         const u32x2 pk = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
         *reinterpret_cast<u32x2*>(op + d0) = pk;
@@ -461,15 +480,15 @@ __global__ __launch_bounds__(kWave) void schedule_kernel(const int32_t* __restri
   if (g == 0) sched->prefix[0] = 0;
 }
 
-template <int D, class Rows, bool kStga>
+template <int D, class Rows, int kEpi>
 int launch_attn(const void* Q, const void* K, const void* V, void* O, int64_t row_stride, float scale,
-                float alpha, float beta, Rows rows, int64_t items_bound, hipStream_t st) {
+                Epilogue epi, Rows rows, int64_t items_bound, hipStream_t st) {
   const int64_t run = (int64_t)kNumXcd * kXcdRun;
   const int64_t grid = ceil_div(items_bound, run) * run;
   if (grid > 0x7fffffff) return MOGA_ERR_SHAPE;
-  attn_kernel<D, kQB, Rows, kStga><<<dim3((unsigned)grid), waves_for<kQB>() * kWave, 0, st>>>(
+  attn_kernel<D, kQB, Rows, kEpi><<<dim3((unsigned)grid), waves_for<kQB>() * kWave, 0, st>>>(
       static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V),
-      static_cast<uint16_t*>(O), row_stride, scale * 1.4426950408889634f, alpha, beta, rows);
+      static_cast<uint16_t*>(O), row_stride, scale * 1.4426950408889634f, epi, rows);
   MOGA_LAUNCH_CHECK();
   return MOGA_OK;
 }
@@ -493,8 +512,9 @@ extern "C" int moga_group_attention(const void* Qp, const void* Kp, const void* 
   MOGA_LAUNCH_CHECK();
   MogaRows rows{cu_seqlens, sched, M, H};
   const int64_t bound = (ceil_div(N, kBM) + M) * H;
-  if (D == 128) return launch_attn<128, MogaRows, false>(Qp, Kp, Vp, Op, (int64_t)H * D, scale, 1.f, 0.f, rows, bound, st);
-  return launch_attn<64, MogaRows, false>(Qp, Kp, Vp, Op, (int64_t)H * D, scale, 1.f, 0.f, rows, bound, st);
+  const Epilogue epi{1.f, 0.f, nullptr, nullptr};
+  if (D == 128) return launch_attn<128, MogaRows, kEpiPlain>(Qp, Kp, Vp, Op, (int64_t)H * D, scale, epi, rows, bound, st);
+  return launch_attn<64, MogaRows, kEpiPlain>(Qp, Kp, Vp, Op, (int64_t)H * D, scale, epi, rows, bound, st);
 }
 
 extern "C" int moga_stga_attention(const void* Q, const void* K, const void* V, int32_t T, int32_t Hs, int32_t Ws,
@@ -514,6 +534,29 @@ extern "C" int moga_stga_attention(const void* Q, const void* K, const void* V, 
   if (items > 0x7fffffff) return MOGA_ERR_SHAPE;
   StgaRows rows{Hs, Ws, win_t, tile_h, tile_w, Hs / tile_h, Ws / tile_w, tpg, H, (int)items};
   hipStream_t st = as_stream(stream);
-  if (D == 128) return launch_attn<128, StgaRows, true>(Q, K, V, O, (int64_t)H * D, scale, alpha, beta, rows, items, st);
-  return launch_attn<64, StgaRows, true>(Q, K, V, O, (int64_t)H * D, scale, alpha, beta, rows, items, st);
+  const Epilogue epi{alpha, beta, nullptr, nullptr};
+  if (D == 128) return launch_attn<128, StgaRows, kEpiScaled>(Q, K, V, O, (int64_t)H * D, scale, epi, rows, items, st);
+  return launch_attn<64, StgaRows, kEpiScaled>(Q, K, V, O, (int64_t)H * D, scale, epi, rows, items, st);
+}
+
+extern "C" int moga_group_attention_unpermute(const void* Qp, const void* Kp, const void* Vp,
+                                              const int32_t* cu_seqlens, const int32_t* perm, const float* gate,
+                                              int64_t N, int32_t H, int32_t D, int32_t M, float softmax_scale,
+                                              float beta, void* O, void* ws, size_t ws_bytes, void* stream) {
+  using namespace moga;
+  if (!Qp || !Kp || !Vp || !cu_seqlens || !perm || !gate || !O) return MOGA_ERR_NULL;
+  if (N < 1 || N >= (int64_t(1) << 31) || M < 1 || H < 1 || D < 1) return MOGA_ERR_SHAPE;
+  if (M > kMaxGroups || !valid_head_dims(H, D)) return MOGA_ERR_UNSUPPORTED;
+  const size_t need = moga_workspace_bytes(MOGA_OP_GROUP_ATTENTION, N, M, H, D);
+  if (!ws || ws_bytes < need) return MOGA_ERR_WORKSPACE;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
+  hipStream_t st = as_stream(stream);
+  auto* sched = static_cast<AttnSchedule*>(ws);
+  schedule_kernel<<<1, kWave, 0, st>>>(cu_seqlens, M, H, sched);
+  MOGA_LAUNCH_CHECK();
+  MogaRows rows{cu_seqlens, sched, M, H};
+  const int64_t bound = (ceil_div(N, kBM) + M) * H;
+  const Epilogue epi{1.f, beta, perm, gate};
+  if (D == 128) return launch_attn<128, MogaRows, kEpiGated>(Qp, Kp, Vp, O, (int64_t)H * D, scale, epi, rows, bound, st);
+  return launch_attn<64, MogaRows, kEpiGated>(Qp, Kp, Vp, O, (int64_t)H * D, scale, epi, rows, bound, st);
 }

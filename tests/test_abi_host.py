@@ -19,8 +19,8 @@ FAKE = ctypes.c_void_p(4096)  # never dereferenced: every call below fails valid
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        from sparse_attention_long_router_amd import build
-        build.build(verbose=False)
+        import __graft_entry__
+        __graft_entry__._load_build_script().build(verbose=False)
     from sparse_attention_long_router_amd import _lib
     return _lib.LIB
 
@@ -33,7 +33,7 @@ def declared_symbols():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     for n in names:
         assert hasattr(lib, n), n
     from sparse_attention_long_router_amd import _lib
@@ -103,6 +103,18 @@ def test_attention_argument_errors(lib):
     assert a(FAKE, FAKE, FAKE, FAKE, 100, 2, 128, 70, 0.0, FAKE, FAKE, nb, None) == EUNSUP
     assert a(FAKE, FAKE, FAKE, FAKE, 100, 2, 128, 4, 0.0, FAKE, None, nb, None) == EWS
     assert a(FAKE, FAKE, FAKE, FAKE, 100, 2, 128, 4, 0.0, FAKE, FAKE, nb - 1, None) == EWS
+
+
+def test_fused_attention_argument_errors(lib):
+    a = lib.moga_group_attention_unpermute
+    nb = lib.moga_workspace_bytes(2, 100, 4, 2, 128)
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 100, 2, 128, 4, 0.0, 0.0, FAKE, FAKE, nb, None]
+    assert a(*args[:4], None, *args[5:]) == ENULL          # perm
+    assert a(*args[:5], None, *args[6:]) == ENULL          # gate
+    assert a(*args[:6], 0, *args[7:]) == ESHAPE            # N
+    assert a(*args[:8], 48, *args[9:]) == EUNSUP           # D
+    assert a(*args[:13], None, *args[14:]) == EWS
+    assert a(*args[:14], nb - 1, None) == EWS
 
 
 def test_unpermute_argument_errors(lib):

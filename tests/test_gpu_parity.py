@@ -63,6 +63,9 @@ def _full_check(moga, inp, bias=None, label=""):
         assert torch.equal(a, b[perm])
     e_attn = assert_output_close(_np(Op), ref["Op"], "Op")
     e_out = assert_output_close(_np(O), ref["O"], "O")
+    Of = moga.moga_group_attention_unpermute(p["Qp"], p["Kp"], p["Vp"], p["cu_seqlens"], p["perm"], gate)
+    torch.cuda.synchronize()
+    assert_output_close(_np(Of), ref["O"], "O (fused attention + unpermute)")
     print(f"[parity] {label} Op {e_attn} O {e_out}", flush=True)
     return gid, gate, p, Op, O, ref
 
@@ -99,6 +102,18 @@ def test_attention_deterministic(moga):
     a = moga.moga_group_attention(p["Qp"], p["Kp"], p["Vp"], p["cu_seqlens"])
     b = moga.moga_group_attention(p["Qp"], p["Kp"], p["Vp"], p["cu_seqlens"])
     assert torch.equal(a, b)
+
+
+def test_fused_unpermute_accumulates(moga):
+    inp = _inputs("wan13b_21f", N=2600, H=2, D=128, M=5, d_model=256)
+    gid, gate = moga.moga_route(inp["X"], inp["Wr"])
+    p = moga.moga_permute(gid, 5, inp["Q"], inp["K"], inp["V"])
+    prev = inp["V"].clone()
+    O = moga.moga_group_attention_unpermute(p["Qp"], p["Kp"], p["Vp"], p["cu_seqlens"], p["perm"], gate,
+                                            beta=0.5, O=prev)
+    torch.cuda.synchronize()
+    ref = oracle.moga_forward(*(_np(inp[k]) for k in ("X", "Wr", "Q", "K", "V")), 5)
+    assert_output_close(_np(O), ref["O"] + 0.5 * _np(inp["V"]), "fused O + 0.5 V")
 
 
 def test_unpermute_accumulate(moga):
