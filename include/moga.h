@@ -54,7 +54,8 @@ typedef enum moga_op {
   MOGA_OP_PERMUTE = 1,
   MOGA_OP_GROUP_ATTENTION = 2,
   MOGA_OP_UNPERMUTE = 3,
-  MOGA_OP_STGA_ATTENTION = 4
+  MOGA_OP_STGA_ATTENTION = 4,
+  MOGA_OP_BALANCE_STATS = 5
 } moga_op;
 
 /*
@@ -150,6 +151,17 @@ int moga_stga_attention(const void* Q, const void* K, const void* V,
                         int32_t T, int32_t Hs, int32_t Ws, int32_t win_t, int32_t tile_h,
                         int32_t tile_w, int32_t H, int32_t D, float softmax_scale,
                         float alpha, float beta, void* O, void* stream);
+
+/*
+ * moga_balance_stats -- router balance statistics (section "Group Balancing
+ *   Loss: Preventing Router Collapse", Eq. 6): F[i] = #{n : group_id[n] = i} / N,
+ *   P[i] = (sum of gate[n] over tokens with group_id[n] = i) / N, and
+ *   loss[0] = alpha * M * sum_i F[i] * P[i].  F, P float [M]; loss float [1]
+ *   (device).  Sums are reduced in a fixed order, so results are
+ *   reproducible bit for bit.  ws: moga_workspace_bytes(MOGA_OP_BALANCE_STATS, ...).
+ */
+int moga_balance_stats(const int32_t* group_id, const float* gate, int64_t N, int32_t M, float alpha,
+                       float* F, float* P, float* loss, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moga_workspace_bytes -- bytes of workspace `op` needs for these sizes

@@ -5,7 +5,7 @@ of include/moga.h); this package is its Python binding.  Importing it fails if
 the library has not been built (`python sparse_attention_long_router_amd/build.py`).
 """
 
-from ._lib import (MOGA_OP_GROUP_ATTENTION, MOGA_OP_PERMUTE, MOGA_OP_ROUTE,  # noqa: F401
-                   MOGA_OP_STGA_ATTENTION, MOGA_OP_UNPERMUTE, LIB_PATH, MogaError, version)
-from .binding import (MogaForward, moga_group_attention, moga_group_attention_unpermute,  # noqa: F401
-                      moga_permute, moga_route, moga_stga_attention, moga_unpermute, moga_workspace_bytes)
+from ._lib import (MOGA_OP_BALANCE_STATS, MOGA_OP_GROUP_ATTENTION, MOGA_OP_PERMUTE,  # noqa: F401
+                   MOGA_OP_ROUTE, MOGA_OP_STGA_ATTENTION, MOGA_OP_UNPERMUTE, LIB_PATH, MogaError, version)
+from .binding import (MogaForward, moga_balance_stats, moga_group_attention,  # noqa: F401
+                      moga_group_attention_unpermute, moga_permute, moga_route, moga_stga_attention, moga_unpermute, moga_workspace_bytes)

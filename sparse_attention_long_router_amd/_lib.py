@@ -20,6 +20,7 @@ MOGA_OP_PERMUTE = 1
 MOGA_OP_GROUP_ATTENTION = 2
 MOGA_OP_UNPERMUTE = 3
 MOGA_OP_STGA_ATTENTION = 4
+MOGA_OP_BALANCE_STATS = 5
 
 # every symbol include/moga.h declares, with its ctypes signature
 _c = ctypes
@@ -34,6 +35,7 @@ SIGNATURES = {
     "moga_unpermute": (_c.c_int, [_vp, _vp, _vp, _i64, _i32, _i32, _f32, _vp, _vp]),
     "moga_stga_attention": (_c.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                                        _f32, _f32, _vp, _vp]),
+    "moga_balance_stats": (_c.c_int, [_vp, _vp, _i64, _i32, _f32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moga_workspace_bytes": (_sz, [_i32, _i64, _i32, _i32, _i32]),
     "moga_strerror": (_c.c_char_p, [_i32]),
     "moga_version": (_i32, []),

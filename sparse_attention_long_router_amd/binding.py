@@ -11,7 +11,7 @@ from __future__ import annotations
 import torch
 
 from . import _lib
-from ._lib import (MOGA_OP_GROUP_ATTENTION, MOGA_OP_PERMUTE, check, ptr, stream_handle)
+from ._lib import (MOGA_OP_BALANCE_STATS, MOGA_OP_GROUP_ATTENTION, MOGA_OP_PERMUTE, check, ptr, stream_handle)
 
 BF16 = torch.bfloat16
 
@@ -169,6 +169,22 @@ def moga_stga_attention(Q, K, V, T, Hs, Ws, win_t, tile_h, tile_w, softmax_scale
                                        float(softmax_scale), float(alpha), float(beta), ptr(O), stream_handle()),
           "moga_stga_attention")
     return O
+
+
+def moga_balance_stats(group_id, gate, M, alpha=0.1, ws=None):
+    """F [M], P [M] and the loss alpha*M*sum(F*P) (float32 device tensors)."""
+    _need(group_id, "group_id", torch.int32, 1)
+    N = group_id.shape[0]
+    _need(gate, "gate", torch.float32, 1, (N,))
+    dev = group_id.device
+    F = torch.empty(M, dtype=torch.float32, device=dev)
+    P = torch.empty(M, dtype=torch.float32, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    ws, nbytes = _workspace(MOGA_OP_BALANCE_STATS, N, M, 1, 64, ws, dev)
+    check(_lib.LIB.moga_balance_stats(ptr(group_id), ptr(gate), N, M, float(alpha), ptr(F), ptr(P), ptr(loss),
+                                      ptr(ws), nbytes, stream_handle()),
+          "moga_balance_stats")
+    return F, P, loss
 
 
 class MogaForward:

@@ -11,6 +11,8 @@ extern "C" size_t moga_workspace_bytes(int32_t op, int64_t N, int32_t M, int32_t
       return align_up(2 * (size_t)M * (size_t)sort_blocks(N) * sizeof(int32_t), 256);
     case MOGA_OP_GROUP_ATTENTION:  // the largest-group-first schedule
       return align_up(sizeof(AttnSchedule), 256);
+    case MOGA_OP_BALANCE_STATS:  // per-(group, block) counts and gate sums
+      return align_up(2 * (size_t)M * (size_t)sort_blocks(N) * 4, 256);
     default:
       return 0;
   }

@@ -33,7 +33,7 @@ def declared_symbols():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(lib, n), n
     from sparse_attention_long_router_amd import _lib
@@ -115,6 +115,17 @@ def test_fused_attention_argument_errors(lib):
     assert a(*args[:8], 48, *args[9:]) == EUNSUP           # D
     assert a(*args[:13], None, *args[14:]) == EWS
     assert a(*args[:14], nb - 1, None) == EWS
+
+
+def test_balance_argument_errors(lib):
+    b = lib.moga_balance_stats
+    nb = lib.moga_workspace_bytes(5, 5000, 8, 1, 64)
+    assert nb >= 2 * 8 * 5 * 4
+    assert b(None, FAKE, 5000, 8, 0.1, FAKE, FAKE, FAKE, FAKE, nb, None) == ENULL
+    assert b(FAKE, FAKE, 5000, 8, 0.1, FAKE, FAKE, None, FAKE, nb, None) == ENULL
+    assert b(FAKE, FAKE, 0, 8, 0.1, FAKE, FAKE, FAKE, FAKE, nb, None) == ESHAPE
+    assert b(FAKE, FAKE, 5000, 65, 0.1, FAKE, FAKE, FAKE, FAKE, nb, None) == EUNSUP
+    assert b(FAKE, FAKE, 5000, 8, 0.1, FAKE, FAKE, FAKE, FAKE, nb - 1, None) == EWS
 
 
 def test_unpermute_argument_errors(lib):

@@ -203,3 +203,21 @@ def test_attention_score_growth(moga, late, label):
     torch.cuda.synchronize()
     ref = oracle.group_attention(_np(Q), _np(K), _np(V), cu.numpy(), 1 / math.sqrt(D))
     assert_output_close(_np(Op), ref, f"Op ({label})")
+
+
+@pytest.mark.parametrize("name,M", [("tiny", 4), ("clip30s_122f", 16), ("minute_372f", 32)])
+def test_balance_stats(moga, name, M):
+    """F_i, P_i and L_gb (Eq. 6) from the GPU route output, against the oracle's
+    float64 statistics of the same group ids and gates; bitwise repeatable."""
+    wl = get_workload(name)
+    print(f"[parity] balance {name}", flush=True)
+    inp = make_inputs(wl, device=DEV)
+    gid, gate = moga.moga_route(inp["X"], inp["Wr"])
+    F, P, loss = moga.moga_balance_stats(gid, gate, wl.M, alpha=0.1)
+    F2, P2, loss2 = moga.moga_balance_stats(gid, gate, wl.M, alpha=0.1)
+    torch.cuda.synchronize()
+    Fr, Pr, Lr = oracle.balance_stats(gid.cpu().numpy(), gate.cpu().numpy(), wl.M, 0.1)
+    np.testing.assert_allclose(F.cpu().numpy(), Fr, rtol=1e-6)
+    np.testing.assert_allclose(P.cpu().numpy(), Pr, rtol=1e-5, atol=1e-9)
+    assert abs(loss.item() - Lr) <= 1e-5 * Lr
+    assert torch.equal(P, P2) and torch.equal(loss, loss2)
