@@ -25,4 +25,9 @@ from .moga_oracle import (  # noqa: F401
     moga_forward,
     moga_output_rows,
     balance_stats,
+    shot_windows,
+    stga_shot_attention,
+    stga_shot_attention_rows,
+    frame_attention,
+    visual_block_forward,
 )

@@ -27,7 +27,13 @@ Readings of points the pages leave open (each is listed in the design doc):
   * empty groups are allowed and produce no rows;
   * the MoGA gate multiplies the attention output once, at unpermute time;
   * STGA groups are fixed (t // win_t, y // tile_h, x // tile_w) windows over
-    frame-major tokens n = (t * Hs + y) * Ws + x, with no gate.
+    frame-major tokens n = (t * Hs + y) * Ws + x, with no gate;
+  * shot-aware STGA: windows restart at every shot start; the keys and values
+    (never the queries) of a shot's first window also hold the previous
+    shot's last frame, those of its last window the next shot's first frame,
+    each restricted to the same spatial tile (shot_windows);
+  * the visual output is the plain mean of MoGA, shot-aware STGA and
+    per-frame attention.
 """
 
 from __future__ import annotations
@@ -50,6 +56,11 @@ __all__ = [
     "moga_forward",
     "moga_output_rows",
     "balance_stats",
+    "shot_windows",
+    "stga_shot_attention",
+    "stga_shot_attention_rows",
+    "frame_attention",
+    "visual_block_forward",
 ]
 
 
@@ -257,6 +268,100 @@ def stga_attention(Q, K, V, T, Hs, Ws, win_t, tile_h, tile_w, scale,
     if beta != 0.0:
         out += beta * _f64(O_prev)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Shot-aware STGA, per-frame attention and the visual block (STGA section)
+# ---------------------------------------------------------------------------
+
+def shot_windows(shot_start, win_t, aug=True):
+    """Temporal windows of the shot-aware STGA.
+
+    STGA section: frames are grouped along time and frames of different shots
+    never share a temporal group; keys and values (not queries) of a group are
+    augmented with latent frames from the adjacent shots.  Reading used: each
+    shot [a_s, a_{s+1}) is cut into consecutive windows of win_t frames (the
+    last one may be shorter); the first window of a shot (other than the first
+    shot) also takes the previous shot's last frame as keys, and the last
+    window of a shot (other than the last shot) the next shot's first frame.
+    Returns a list of (t0, nt, prev_frame or -1, next_frame or -1).
+    """
+    a = [int(x) for x in shot_start]
+    out = []
+    for sh in range(len(a) - 1):
+        lo, hi = a[sh], a[sh + 1]
+        starts = list(range(lo, hi, win_t))
+        for k, t0 in enumerate(starts):
+            nt = min(win_t, hi - t0)
+            prev = lo - 1 if (aug and k == 0 and sh > 0) else -1
+            nxt = hi if (aug and k == len(starts) - 1 and sh < len(a) - 2) else -1
+            out.append((t0, nt, prev, nxt))
+    return out
+
+
+def stga_shot_attention(Q, K, V, T, Hs, Ws, shot_start, win_t, tile_h, tile_w, scale, aug=True):
+    """Shot-aware STGA over frame-major tokens (float64 [N, H, D]): for each
+    window and spatial tile, the window's tokens in the tile attend to those
+    same tokens plus, as extra keys, the tile's tokens in the augmentation
+    frames (shot_windows)."""
+    if Hs % tile_h or Ws % tile_w:
+        raise ValueError("spatial tiles must tile the frame")
+    def tokens(frames, y0, x0):
+        return np.array([(t * Hs + y) * Ws + x for t in frames
+                         for y in range(y0, y0 + tile_h) for x in range(x0, x0 + tile_w)], dtype=np.int64)
+    out = np.zeros(Q.shape, dtype=np.float64)
+    for t0, nt, prev, nxt in shot_windows(shot_start, win_t, aug):
+        extra = [f for f in (prev, nxt) if f >= 0]
+        for y0 in range(0, Hs, tile_h):
+            for x0 in range(0, Ws, tile_w):
+                q_tok = tokens(range(t0, t0 + nt), y0, x0)
+                k_tok = np.concatenate([q_tok, tokens(extra, y0, x0)]) if extra else q_tok
+                for h in range(Q.shape[1]):
+                    q = _f64(Q[q_tok, h, :])
+                    k = _f64(K[k_tok, h, :])
+                    v = _f64(V[k_tok, h, :])
+                    out[q_tok, h, :] = _softmax_rows_times_v((q @ k.T) * scale, v)
+    return out
+
+
+def stga_shot_attention_rows(Q, K, V, T, Hs, Ws, shot_start, win_t, tile_h, tile_w, scale, rows, aug=True):
+    """Shot-aware STGA output of selected tokens only (float64 [len(rows), H, D]);
+    the same windows and key sets as stga_shot_attention."""
+    area = tile_h * tile_w
+    wins = shot_windows(shot_start, win_t, aug)
+    frame_win = {}
+    for t0, nt, prev, nxt in wins:
+        for t in range(t0, t0 + nt):
+            frame_win[t] = (t0, nt, prev, nxt)
+    out = np.zeros((len(rows), Q.shape[1], Q.shape[2]), dtype=np.float64)
+    for a, n in enumerate(np.asarray(rows, dtype=np.int64)):
+        t, y, x = int(n) // (Hs * Ws), (int(n) // Ws) % Hs, int(n) % Ws
+        t0, nt, prev, nxt = frame_win[t]
+        y0, x0 = y // tile_h * tile_h, x // tile_w * tile_w
+        frames = list(range(t0, t0 + nt)) + [f for f in (prev, nxt) if f >= 0]
+        k_tok = np.array([(f * Hs + yy) * Ws + xx for f in frames
+                          for yy in range(y0, y0 + tile_h) for xx in range(x0, x0 + tile_w)], dtype=np.int64)
+        assert k_tok.size == len(frames) * area
+        for h in range(Q.shape[1]):
+            q = _f64(Q[n, h, :])[None, :]
+            out[a, h, :] = _softmax_rows_times_v((q @ _f64(K[k_tok, h, :]).T) * scale, _f64(V[k_tok, h, :]))[0]
+    return out
+
+
+def frame_attention(Q, K, V, T, Hs, Ws, scale):
+    """Per-frame attention (STGA section): every latent frame is one group."""
+    return stga_attention(Q, K, V, T, Hs, Ws, 1, Hs, Ws, scale)
+
+
+def visual_block_forward(X, Wr, Q, K, V, M, T, Hs, Ws, shot_start, win_t, tile_h, tile_w, scale=None, aug=True):
+    """Visual attention output of the STGA section: the arithmetic mean of the
+    MoGA, shot-aware STGA and per-frame attention outputs (float64)."""
+    D = Q.shape[2]
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    moga = moga_forward(X, Wr, Q, K, V, M, scale)["O"]
+    stga = stga_shot_attention(Q, K, V, T, Hs, Ws, shot_start, win_t, tile_h, tile_w, scale, aug)
+    frame = frame_attention(Q, K, V, T, Hs, Ws, scale)
+    return (moga + stga + frame) / 3.0
 
 
 # ---------------------------------------------------------------------------

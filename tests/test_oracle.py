@@ -319,6 +319,93 @@ def test_moga_plus_stga_is_sum_of_branches():
     np.testing.assert_allclose(out["O"], 0.5 * moga + 0.5 * stga, atol=1e-6)
 
 
+def test_shot_windows_hand_example():
+    # 10 frames, shots [0,4) [4,5) [5,10), windows of 3 frames
+    w = oracle.shot_windows([0, 4, 5, 10], 3)
+    assert w == [(0, 3, -1, -1), (3, 1, -1, 4), (4, 1, 3, 5), (5, 3, 4, -1), (8, 2, -1, -1)]
+    assert oracle.shot_windows([0, 4, 5, 10], 3, aug=False) == [(0, 3, -1, -1), (3, 1, -1, -1), (4, 1, -1, -1),
+                                                                (5, 3, -1, -1), (8, 2, -1, -1)]
+
+
+def _shot_mask(T, Hs, Ws, shot_start, win_t, th, tw):
+    """Allowed (query, key) pairs restated token by token from the STGA rules."""
+    N = T * Hs * Ws
+    shot = np.zeros(T, int)
+    for s_, (lo, hi) in enumerate(zip(shot_start[:-1], shot_start[1:])):
+        shot[lo:hi] = s_
+    def win(t):  # index of t's window inside its shot, and whether first/last
+        lo, hi = shot_start[shot[t]], shot_start[shot[t] + 1]
+        k = (t - lo) // win_t
+        return k, k == 0, lo + (k + 1) * win_t >= hi
+    mask = np.zeros((N, N), bool)
+    for n in range(N):
+        t, y, x = n // (Hs * Ws), (n // Ws) % Hs, n % Ws
+        for m in range(N):
+            u, yy, xx = m // (Hs * Ws), (m // Ws) % Hs, m % Ws
+            if yy // th != y // th or xx // tw != x // tw:
+                continue
+            same = shot[u] == shot[t] and win(u)[0] == win(t)[0]
+            k, first, last = win(t)
+            prev = first and shot[t] > 0 and u == shot_start[shot[t]] - 1
+            nxt = last and shot[t] < len(shot_start) - 2 and u == shot_start[shot[t] + 1]
+            mask[n, m] = same or prev or nxt
+    return mask
+
+
+def check_stga_shot_masked():
+    r = _rng(19)
+    T, Hs, Ws, H, D = 7, 2, 4, 2, 8
+    shots = [0, 3, 4, 7]
+    N = T * Hs * Ws
+    Q, K, V = (r.standard_normal((N, H, D)) for _ in range(3))
+    out = oracle.stga_shot_attention(Q, K, V, T, Hs, Ws, shots, 2, 1, 2, 0.3)
+    ref = _sdpa(Q, K, V, _shot_mask(T, Hs, Ws, shots, 2, 1, 2), scale=0.3)
+    np.testing.assert_allclose(out, ref, atol=1e-12)
+    # one shot and windows that tile it: the plain STGA windows
+    plain = oracle.stga_shot_attention(Q, K, V, T, Hs, Ws, [0, T], 7, 2, 2, 0.3)
+    np.testing.assert_allclose(plain, _sdpa(Q, K, V, oracle.stga_group_ids(T, Hs, Ws, 7, 2, 2)[:, None]
+                                             == oracle.stga_group_ids(T, Hs, Ws, 7, 2, 2)[None, :], scale=0.3),
+                               atol=1e-12)
+
+
+def test_stga_shot_is_masked_attention():
+    check_stga_shot_masked()
+
+
+def test_stga_shot_rows_match_masked_attention():
+    r = _rng(21)
+    T, Hs, Ws, H, D = 6, 2, 2, 1, 4
+    shots = [0, 1, 4, 6]
+    N = T * Hs * Ws
+    Q, K, V = (r.standard_normal((N, H, D)) for _ in range(3))
+    for aug in (True, False):
+        rows = oracle.stga_shot_attention_rows(Q, K, V, T, Hs, Ws, shots, 2, 2, 1, 0.7, np.arange(N), aug)
+        mask = _shot_mask(T, Hs, Ws, shots, 2, 2, 1)
+        if not aug:
+            wid = np.array([w for w, (t0, nt, _, _) in enumerate(oracle.shot_windows(shots, 2, False))
+                            for _ in range(nt)])
+            tok_t = np.arange(N) // (Hs * Ws)
+            col = np.arange(N) % Ws
+            mask = (wid[tok_t][:, None] == wid[tok_t][None, :]) & (col[:, None] == col[None, :])
+        np.testing.assert_allclose(rows, _sdpa(Q, K, V, mask, scale=0.7), atol=1e-12)
+
+
+def test_frame_attention_and_visual_mean():
+    r = _rng(20)
+    T, Hs, Ws, H, D, d, M = 4, 2, 3, 2, 8, 12, 3
+    N = T * Hs * Ws
+    X = r.standard_normal((N, d))
+    Wr = r.standard_normal((M, d))
+    Q, K, V = (r.standard_normal((N, H, D)) for _ in range(3))
+    frame_ids = np.arange(N) // (Hs * Ws)
+    fr = oracle.frame_attention(Q, K, V, T, Hs, Ws, 1 / math.sqrt(D))
+    np.testing.assert_allclose(fr, _sdpa(Q, K, V, frame_ids[:, None] == frame_ids[None, :]), atol=1e-12)
+    vb = oracle.visual_block_forward(X, Wr, Q, K, V, M, T, Hs, Ws, [0, 2, 4], 2, 1, 3)
+    moga = oracle.moga_forward(X, Wr, Q, K, V, M)["O"]
+    st = oracle.stga_shot_attention(Q, K, V, T, Hs, Ws, [0, 2, 4], 2, 1, 3, 1 / math.sqrt(D))
+    np.testing.assert_allclose(vb, (moga + st + fr) / 3, atol=1e-12)
+
+
 # ---------------------------------------------------------------------------
 # Group-balancing statistics (Eq. 6)
 # ---------------------------------------------------------------------------
@@ -376,8 +463,19 @@ def _off_by_one_cu(group_id, M):
     return perm, cu, mx
 
 
+def _windows_ignore_shots(shot_start, win_t, aug=True):
+    return _orig_shot_windows([shot_start[0], shot_start[-1]], win_t, aug)
+
+
+def _augment_wrong_frames(shot_start, win_t, aug=True):
+    # the adjacent frames taken one step too far into the neighbouring shots
+    return [(t0, nt, p - 1 if p > 0 else p, n + 1 if 0 <= n < shot_start[-1] - 1 else n)
+            for t0, nt, p, n in _orig_shot_windows(shot_start, win_t, aug)]
+
+
 _orig_permute = om.permute
 _orig_unpermute = om.unpermute
+_orig_shot_windows = om.shot_windows
 
 MUTANTS = [
     ("_softmax_rows_times_v", _wrong_scale, [check_moga_is_gated_masked_attention, check_bruteforce_loops]),
@@ -386,6 +484,8 @@ MUTANTS = [
     ("permute", _unstable_permute, [check_permute_hand_example, check_permute_bruteforce]),
     ("permute", _off_by_one_cu, [check_moga_is_gated_masked_attention]),
     ("unpermute", _ungated_unpermute, [check_moga_is_gated_masked_attention, check_bruteforce_loops]),
+    ("shot_windows", _windows_ignore_shots, [check_stga_shot_masked]),
+    ("shot_windows", _augment_wrong_frames, [check_stga_shot_masked]),
 ]
 
 

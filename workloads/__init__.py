@@ -6,4 +6,4 @@ computes none of the method (no routing decision, sort, attention or gate).
 """
 
 from .configs import WORKLOADS, Workload, get_workload  # noqa: F401
-from .gen import make_inputs, top2_margin, sample_rows  # noqa: F401
+from .gen import make_inputs, make_shots, top2_margin, sample_rows  # noqa: F401

@@ -130,6 +130,18 @@ def make_inputs(wl: Workload, device="cpu", seed: int | None = None, **overrides
     return {"X": Xb, "Wr": Wr, "Q": Q, "K": K, "V": V, "labels": labels, "workload": wl, "seed": seed}
 
 
+def make_shots(T: int, seed: int, min_len: int = 12, max_len: int = 60) -> list:
+    """Seeded multi-shot layout of T latent frames: shot lengths drawn
+    uniformly from [min_len, max_len] latent frames (about 2 to 10 seconds at
+    the 4x temporal compression of a 24 fps video), the last shot cut at T.
+    Returns the shot start frames followed by T (n_shots + 1 values)."""
+    rng = np.random.default_rng(seed * 1000 + 11)
+    starts = [0]
+    while starts[-1] < T:
+        starts.append(min(T, starts[-1] + int(rng.integers(min_len, max_len + 1))))
+    return starts
+
+
 def to_numpy_f32(t: torch.Tensor) -> np.ndarray:
     """Exact float32 copy of a bf16/float tensor on the host."""
     return t.detach().float().cpu().numpy()
