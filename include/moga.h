@@ -153,6 +153,37 @@ int moga_stga_attention(const void* Q, const void* K, const void* V,
                         float alpha, float beta, void* O, void* stream);
 
 /*
+ * moga_stga_shot_attention -- the shot-aware STGA branch (section "Spatial-
+ *   Temporal Group Attention (STGA)": frames of different shots never share a
+ *   temporal group; keys and values, not queries, are augmented with latent
+ *   frames of the adjacent shots).  Frame-major tokens as in
+ *   moga_stga_attention.  Every shot [shot_start[s], shot_start[s+1]) is cut
+ *   into windows of win_t frames, the last one shorter if the shot length is
+ *   not a multiple of win_t.  The queries of a window are its frames' tokens
+ *   inside one tile_h x tile_w spatial tile; its keys and values are those
+ *   tokens, plus (augment != 0) the same tile of the previous shot's last
+ *   frame for the shot's first window and of the next shot's first frame for
+ *   the shot's last window.  O[n] = beta * O[n] + alpha * STGA(n).
+ *   shot_start: DEVICE int32 [n_shots + 1], 0 = shot_start[0] < ... <
+ *   shot_start[n_shots] = T (not checked on the host; boundaries outside
+ *   that order give unspecified output for the affected frames, never an
+ *   out-of-bounds access).  tile_h, tile_w must divide Hs, Ws and
+ *   (win_t + 2) * tile_h * tile_w must be at most 2^20.
+ *   ws: device workspace of moga_stga_shot_workspace_bytes(T, n_shots, win_t)
+ *   bytes (the window table, rebuilt on every call).
+ */
+int moga_stga_shot_attention(const void* Q, const void* K, const void* V,
+                             int32_t T, int32_t Hs, int32_t Ws, const int32_t* shot_start,
+                             int32_t n_shots, int32_t win_t, int32_t tile_h, int32_t tile_w,
+                             int32_t augment, int32_t H, int32_t D, float softmax_scale,
+                             float alpha, float beta, void* O, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/* moga_stga_shot_workspace_bytes -- workspace of moga_stga_shot_attention;
+ *   0 for invalid sizes.  Host-only, no device call. */
+size_t moga_stga_shot_workspace_bytes(int32_t T, int32_t n_shots, int32_t win_t);
+
+/*
  * moga_balance_stats -- router balance statistics (section "Group Balancing
  *   Loss: Preventing Router Collapse", Eq. 6): F[i] = #{n : group_id[n] = i} / N,
  *   P[i] = (sum of gate[n] over tokens with group_id[n] = i) / N, and

@@ -35,6 +35,9 @@ SIGNATURES = {
     "moga_unpermute": (_c.c_int, [_vp, _vp, _vp, _i64, _i32, _i32, _f32, _vp, _vp]),
     "moga_stga_attention": (_c.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                                        _f32, _f32, _vp, _vp]),
+    "moga_stga_shot_attention": (_c.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
+                                            _i32, _i32, _f32, _f32, _f32, _vp, _vp, _sz, _vp]),
+    "moga_stga_shot_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "moga_balance_stats": (_c.c_int, [_vp, _vp, _i64, _i32, _f32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moga_workspace_bytes": (_sz, [_i32, _i64, _i32, _i32, _i32]),
     "moga_strerror": (_c.c_char_p, [_i32]),

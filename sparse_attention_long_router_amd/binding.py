@@ -171,6 +171,41 @@ def moga_stga_attention(Q, K, V, T, Hs, Ws, win_t, tile_h, tile_w, softmax_scale
     return O
 
 
+def moga_stga_shot_workspace_bytes(T: int, n_shots: int, win_t: int) -> int:
+    return int(_lib.LIB.moga_stga_shot_workspace_bytes(T, n_shots, win_t))
+
+
+def moga_stga_shot_attention(Q, K, V, T, Hs, Ws, shot_start, win_t, tile_h, tile_w, augment=True,
+                             softmax_scale=0.0, alpha=1.0, beta=0.0, O=None, ws=None):
+    """Shot-aware window attention over frame-major tokens; O = beta*O + alpha*STGA.
+    shot_start: int32 GPU tensor [n_shots + 1] (0, ..., T)."""
+    _need(Q, "Q", BF16, 3)
+    N, H, D = Q.shape
+    _need(K, "K", BF16, 3, Q.shape)
+    _need(V, "V", BF16, 3, Q.shape)
+    _need(shot_start, "shot_start", torch.int32, 1)
+    n_shots = shot_start.shape[0] - 1
+    if O is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs an existing O")
+        O = torch.empty_like(Q)
+    _need(O, "O", BF16, 3, Q.shape)
+    if T * Hs * Ws != N:
+        raise ValueError("T*Hs*Ws must equal N")
+    if n_shots < 1:
+        raise ValueError("shot_start needs at least two entries")
+    need = moga_stga_shot_workspace_bytes(T, n_shots, win_t)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=Q.device)
+    _need(ws, "ws")
+    check(_lib.LIB.moga_stga_shot_attention(ptr(Q), ptr(K), ptr(V), T, Hs, Ws, ptr(shot_start), n_shots, win_t,
+                                            tile_h, tile_w, int(bool(augment)), H, D, float(softmax_scale),
+                                            float(alpha), float(beta), ptr(O), ptr(ws),
+                                            ws.numel() * ws.element_size(), stream_handle()),
+          "moga_stga_shot_attention")
+    return O
+
+
 def moga_balance_stats(group_id, gate, M, alpha=0.1, ws=None):
     """F [M], P [M] and the loss alpha*M*sum(F*P) (float32 device tensors)."""
     _need(group_id, "group_id", torch.int32, 1)
@@ -190,9 +225,16 @@ def moga_balance_stats(group_id, gate, M, alpha=0.1, ws=None):
 class MogaForward:
     """Preallocated buffers for one MoGA layer pass (route, permute, group
     attention and gated unpermute -- fused into one kernel unless
-    ``fused=False`` -- and, when ``stga`` geometry is given, the STGA sum).
+    ``fused=False`` -- and, when ``stga`` geometry is given, the STGA branch).
     ``__call__`` launches the library calls back to back on the current
-    stream and allocates nothing."""
+    stream and allocates nothing.
+
+    ``stga``: dict with T, Hs, Ws, win_t, tile_h, tile_w and optionally
+    ``shot_start`` (a list of shot start frames ending with T) and ``augment``.
+    Without shots the branch is the plain static-window STGA, added with
+    ``stga_weight``.  With ``shot_start`` the pass computes the visual
+    attention output of the STGA section: the mean of MoGA, shot-aware STGA
+    and per-frame attention."""
 
     def __init__(self, N, d_model, H, D, M, device, stga=None, fused=True):
         self.N, self.d_model, self.H, self.D, self.M, self.stga = N, d_model, H, D, M, stga
@@ -200,15 +242,23 @@ class MogaForward:
         e = lambda *s, dt=BF16: torch.empty(*s, dtype=dt, device=device)  # noqa: E731
         self.group_id = e(N, dt=torch.int32)
         self.gate = e(N, dt=torch.float32)
-        self.Qp, self.Kp, self.Vp, self.Op, self.O = (e(N, H, D) for _ in range(5))
+        self.Qp, self.Kp, self.Vp, self.O = (e(N, H, D) for _ in range(4))
+        self.Op = None if fused else e(N, H, D)
         self.perm = e(N, dt=torch.int32)
         self.cu_seqlens = e(M + 1, dt=torch.int32)
         self.max_seqlen = e(1, dt=torch.int32)
         self.ws_perm = e(max(moga_workspace_bytes(MOGA_OP_PERMUTE, N, M, H, D), 1), dt=torch.uint8)
         self.ws_attn = e(max(moga_workspace_bytes(MOGA_OP_GROUP_ATTENTION, N, M, H, D), 1), dt=torch.uint8)
+        self.shot_start = None
+        if stga is not None and stga.get("shot_start") is not None:
+            shots = list(stga["shot_start"])
+            self.shot_start = torch.tensor(shots, dtype=torch.int32).to(device)
+            self.ws_shot = e(max(moga_stga_shot_workspace_bytes(stga["T"], len(shots) - 1, stga["win_t"]), 1),
+                             dt=torch.uint8)
 
     def __call__(self, X, Wr, Q, K, V, bias=None, softmax_scale=0.0, stga_weight=1.0, moga_weight=1.0):
-        """O = moga_weight * MoGA + stga_weight * STGA (the STGA term only with geometry)."""
+        """O = moga_weight * MoGA + stga_weight * STGA (the STGA term only with
+        geometry); with shots, O = (MoGA + shot STGA + per-frame) / 3."""
         moga_route(X, Wr, bias, self.group_id, self.gate)
         moga_permute(self.group_id, self.M, Q, K, V, self.Qp, self.Kp, self.Vp, self.perm, self.cu_seqlens,
                      self.max_seqlen, self.ws_perm)
@@ -218,10 +268,19 @@ class MogaForward:
         else:
             moga_group_attention(self.Qp, self.Kp, self.Vp, self.cu_seqlens, softmax_scale, self.Op, self.ws_attn)
             moga_unpermute(self.Op, self.perm, self.gate, 0.0, self.O)
-        if self.stga is not None:
-            g = self.stga
+        g = self.stga
+        if g is None:
+            if moga_weight != 1.0:
+                raise ValueError("moga_weight applies only together with an STGA branch")
+        elif self.shot_start is not None:
+            third = 1.0 / 3.0
+            # O = MoGA  ->  (MoGA + shot STGA) / 3  ->  + per-frame / 3
+            moga_stga_shot_attention(Q, K, V, g["T"], g["Hs"], g["Ws"], self.shot_start, g["win_t"], g["tile_h"],
+                                     g["tile_w"], g.get("augment", True), softmax_scale, third, third, self.O,
+                                     self.ws_shot)
+            moga_stga_attention(Q, K, V, g["T"], g["Hs"], g["Ws"], 1, g["Hs"], g["Ws"], softmax_scale, third, 1.0,
+                                self.O)
+        else:
             moga_stga_attention(Q, K, V, g["T"], g["Hs"], g["Ws"], g["win_t"], g["tile_h"], g["tile_w"],
                                 softmax_scale, stga_weight, moga_weight, self.O)
-        elif moga_weight != 1.0:
-            raise ValueError("moga_weight applies only together with an STGA branch")
         return self.O

@@ -51,11 +51,13 @@ constexpr int kXcdRun = 8;                          // consecutive items per XCD
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 struct Work {
-  int len;      // group size
+  int len;      // keys of the group
+  int nq;       // queries of the group (= len except for shot-aware windows)
   int q0;       // first query (group-local) of this item
   int head;
   int64_t row0; // MoGA: first permuted row of the group
   int t0, y0, x0;  // STGA: window origin
+  int nt, e0, e1;  // shot-aware STGA: window frames, extra key frames (-1: none)
 };
 
 // Learned groups: rows of group g are cu[g] .. cu[g+1]-1 of the permuted tensors.
@@ -74,12 +76,14 @@ struct MogaRows {
     const int len = cu[g + 1] - lo;
     const int nt = (len + kBM - 1) / kBM;
     w.len = len;
+    w.nq = len;
     w.head = local / nt;
     w.q0 = (local - w.head * nt) * kBM;
     w.row0 = lo;
     return true;
   }
   __device__ __forceinline__ int64_t row(const Work& w, int i) const { return w.row0 + i; }
+  __device__ __forceinline__ int64_t key(const Work& w, int i) const { return w.row0 + i; }
 };
 
 // Static windows over frame-major tokens n = (t*Hs + y)*Ws + x.
@@ -93,6 +97,7 @@ struct StgaRows {
     w.head = rem / tiles_per_group;
     w.q0 = (rem - w.head * tiles_per_group) * kBM;
     w.len = win_t * tile_h * tile_w;
+    w.nq = w.len;
     const int tw = grp / (nty * ntx);
     const int r2 = grp - tw * (nty * ntx);
     const int ty = r2 / ntx;
@@ -109,6 +114,64 @@ struct StgaRows {
     const int yy = rem / tile_w;
     const int xx = rem - yy * tile_w;
     return ((int64_t)(w.t0 + tt) * Hs + (w.y0 + yy)) * Ws + (w.x0 + xx);
+  }
+  __device__ __forceinline__ int64_t key(const Work& w, int i) const { return row(w, i); }
+};
+
+// One temporal window of the shot-aware STGA: frames t0 .. t0+nt-1 of one
+// shot, plus the frames prev / next of the neighbouring shots (-1: none)
+// whose tokens join the keys and values only.
+struct ShotWindow {
+  int t0, nt, prev, next;
+};
+
+// Shot-aware windows: queries are the window's own frames inside one spatial
+// tile; keys are those tokens followed by the same tile of the extra frames.
+// Items: window-major, then spatial tile, head and query tile, so the query
+// tiles sharing one key set are consecutive (and land on one XCD).
+struct ShotRows {
+  const ShotWindow* win;
+  const int* nwin;
+  int Hs, Ws, tile_h, tile_w, ntx, nspatial, tpg, H;
+  __device__ __forceinline__ bool decode(int item, Work& w) const {
+    const int per_win = nspatial * H * tpg;
+    const int wi = item / per_win;
+    if (wi >= *nwin) return false;
+    int rem = item - wi * per_win;
+    const int sp = rem / (H * tpg);
+    rem -= sp * (H * tpg);
+    w.head = rem / tpg;
+    w.q0 = (rem - w.head * tpg) * kBM;
+    const ShotWindow sw = win[wi];
+    const int area = tile_h * tile_w;
+    w.nq = sw.nt * area;
+    if (w.q0 >= w.nq) return false;
+    w.nt = sw.nt;
+    w.e0 = sw.prev >= 0 ? sw.prev : sw.next;
+    w.e1 = sw.prev >= 0 ? sw.next : -1;
+    w.len = (sw.nt + (w.e0 >= 0) + (w.e1 >= 0)) * area;
+    w.t0 = sw.t0;
+    const int ty = sp / ntx;
+    w.y0 = ty * tile_h;
+    w.x0 = (sp - ty * ntx) * tile_w;
+    w.row0 = 0;
+    return true;
+  }
+  __device__ __forceinline__ int64_t at(const Work& w, int frame, int i) const {
+    const int yy = i / tile_w;
+    const int xx = i - yy * tile_w;
+    return ((int64_t)frame * Hs + (w.y0 + yy)) * Ws + (w.x0 + xx);
+  }
+  __device__ __forceinline__ int64_t row(const Work& w, int i) const {
+    const int area = tile_h * tile_w;
+    const int tt = i / area;
+    return at(w, w.t0 + tt, i - tt * area);
+  }
+  __device__ __forceinline__ int64_t key(const Work& w, int i) const {
+    const int area = tile_h * tile_w;
+    const int tt = i / area;
+    const int frame = tt < w.nt ? w.t0 + tt : (tt == w.nt ? w.e0 : w.e1);
+    return at(w, frame, i - tt * area);
   }
 };
 
@@ -157,7 +220,7 @@ __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ K, const
     const int r = q / CPR, p = q % CPR;
     int key = k0 + r;
     key = key < w.len ? key : w.len - 1;
-    const int64_t base = rows.row(w, key) * row_stride + hoff;
+    const int64_t base = rows.key(w, key) * row_stride + hoff;
     const int lds_off = (wave * LOADS + j) * kWave * 8;  // uint16 elements, wave-uniform
     __builtin_amdgcn_global_load_lds((global_void*)(K + base + (p ^ kswz(r, CPR)) * 8), (lds_void*)(Ks + lds_off),
                                      16, 0, 0);
@@ -333,8 +396,8 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave) void attn_kernel(
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
     const int qi = w.q0 + (wave * QB + b) * 32 + c;
-    qvalid[b] = qi < w.len;
-    qrow[b] = rows.row(w, qvalid[b] ? qi : w.len - 1);
+    qvalid[b] = qi < w.nq;
+    qrow[b] = rows.row(w, qvalid[b] ? qi : w.nq - 1);
     const uint16_t* qp = Q + qrow[b] * row_stride + hoff + 8 * hh;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) qf[b][s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
@@ -480,6 +543,52 @@ __global__ __launch_bounds__(kWave) void schedule_kernel(const int32_t* __restri
   if (g == 0) sched->prefix[0] = 0;
 }
 
+// Window table of the shot-aware STGA, one workgroup: every shot
+// [shot_start[s], shot_start[s+1]) is cut into windows of win_t frames (the
+// last one shorter if needed); the shot's first window gets the previous
+// shot's last frame as extra keys, its last window the next shot's first
+// frame.  Boundaries are clamped into [0, T] and at most max_windows entries
+// are written, so malformed boundaries cannot write out of bounds.
+constexpr int kShotThreads = 256;
+__global__ __launch_bounds__(kShotThreads) void shot_windows_kernel(const int32_t* __restrict__ shot_start,
+                                                                  int n_shots, int T, int win_t, int augment,
+                                                                  int max_windows, ShotWindow* __restrict__ win,
+                                                                  int* __restrict__ nwin) {
+  __shared__ int scan[kShotThreads];
+  const int tid = threadIdx.x;
+  int base = 0;
+  for (int s0 = 0; s0 < n_shots; s0 += kShotThreads) {
+    const int s = s0 + tid;
+    int lo = 0, hi = 0, cnt = 0;
+    if (s < n_shots) {
+      lo = min(max(shot_start[s], 0), T);
+      hi = min(max(shot_start[s + 1], lo), T);
+      cnt = (hi - lo + win_t - 1) / win_t;
+    }
+    scan[tid] = cnt;
+    __syncthreads();
+    for (int off = 1; off < kShotThreads; off <<= 1) {
+      const int v = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    const int first = base + scan[tid] - cnt;
+    for (int k = 0; k < cnt && first + k < max_windows; ++k) {
+      const int t0 = lo + k * win_t;
+      ShotWindow sw;
+      sw.t0 = t0;
+      sw.nt = min(win_t, hi - t0);
+      sw.prev = (augment && k == 0 && s > 0 && lo > 0) ? lo - 1 : -1;
+      sw.next = (augment && k == cnt - 1 && s + 1 < n_shots && hi < T) ? hi : -1;
+      win[first + k] = sw;
+    }
+    base += scan[kShotThreads - 1];
+    __syncthreads();
+  }
+  if (tid == 0) *nwin = min(base, max_windows);
+}
+
 template <int D, class Rows, int kEpi>
 int launch_attn(const void* Q, const void* K, const void* V, void* O, int64_t row_stride, float scale,
                 Epilogue epi, Rows rows, int64_t items_bound, hipStream_t st) {
@@ -559,4 +668,44 @@ extern "C" int moga_group_attention_unpermute(const void* Qp, const void* Kp, co
   const Epilogue epi{1.f, beta, perm, gate};
   if (D == 128) return launch_attn<128, MogaRows, kEpiGated>(Qp, Kp, Vp, O, (int64_t)H * D, scale, epi, rows, bound, st);
   return launch_attn<64, MogaRows, kEpiGated>(Qp, Kp, Vp, O, (int64_t)H * D, scale, epi, rows, bound, st);
+}
+
+extern "C" size_t moga_stga_shot_workspace_bytes(int32_t T, int32_t n_shots, int32_t win_t) {
+  if (T < 1 || n_shots < 1 || win_t < 1) return 0;
+  const int64_t max_windows = moga::ceil_div(T, win_t) + n_shots;
+  return 256 + (size_t)max_windows * sizeof(moga::ShotWindow);
+}
+
+extern "C" int moga_stga_shot_attention(const void* Q, const void* K, const void* V, int32_t T, int32_t Hs,
+                                        int32_t Ws, const int32_t* shot_start, int32_t n_shots, int32_t win_t,
+                                        int32_t tile_h, int32_t tile_w, int32_t augment, int32_t H, int32_t D,
+                                        float softmax_scale, float alpha, float beta, void* O, void* ws,
+                                        size_t ws_bytes, void* stream) {
+  using namespace moga;
+  if (!Q || !K || !V || !O || !shot_start) return MOGA_ERR_NULL;
+  if (T < 1 || Hs < 1 || Ws < 1 || n_shots < 1 || win_t < 1 || tile_h < 1 || tile_w < 1 || H < 1 || D < 1)
+    return MOGA_ERR_SHAPE;
+  if (n_shots > T || Hs % tile_h || Ws % tile_w) return MOGA_ERR_SHAPE;
+  const int64_t N = (int64_t)T * Hs * Ws;
+  const int64_t area = (int64_t)tile_h * tile_w;
+  if (N >= (int64_t(1) << 31)) return MOGA_ERR_SHAPE;
+  if ((int64_t)(win_t + 2) * area > (int64_t(1) << 20) || !valid_head_dims(H, D)) return MOGA_ERR_UNSUPPORTED;
+  const size_t need = moga_stga_shot_workspace_bytes(T, n_shots, win_t);
+  if (!ws || ws_bytes < need) return MOGA_ERR_WORKSPACE;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
+  const int max_windows = (int)(ceil_div(T, win_t) + n_shots);
+  const int tpg = (int)ceil_div((int64_t)win_t * area, kBM);
+  const int ntx = Ws / tile_w, nspatial = (Hs / tile_h) * ntx;
+  const int64_t items = (int64_t)max_windows * nspatial * H * tpg;
+  if (items > 0x7fffffff) return MOGA_ERR_SHAPE;
+  hipStream_t st = as_stream(stream);
+  int* nwin = static_cast<int*>(ws);
+  auto* win = reinterpret_cast<ShotWindow*>(static_cast<char*>(ws) + 256);
+  shot_windows_kernel<<<1, kShotThreads, 0, st>>>(shot_start, n_shots, T, win_t, augment != 0, max_windows, win,
+                                                  nwin);
+  MOGA_LAUNCH_CHECK();
+  ShotRows rows{win, nwin, Hs, Ws, tile_h, tile_w, ntx, nspatial, tpg, H};
+  const Epilogue epi{alpha, beta, nullptr, nullptr};
+  if (D == 128) return launch_attn<128, ShotRows, kEpiScaled>(Q, K, V, O, (int64_t)H * D, scale, epi, rows, items, st);
+  return launch_attn<64, ShotRows, kEpiScaled>(Q, K, V, O, (int64_t)H * D, scale, epi, rows, items, st);
 }

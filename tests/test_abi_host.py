@@ -33,7 +33,7 @@ def declared_symbols():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), n
     from sparse_attention_long_router_amd import _lib
@@ -145,3 +145,22 @@ def test_stga_argument_errors(lib):
     assert s(FAKE, FAKE, FAKE, 0, 30, 52, 1, 30, 26, 2, 128, 0.0, 1.0, 0.0, FAKE, None) == ESHAPE
     assert s(FAKE, FAKE, FAKE, 6, 30, 52, 3, 30, 26, 2, 100, 0.0, 1.0, 0.0, FAKE, None) == EUNSUP
     assert s(FAKE, FAKE, FAKE, 2048, 1024, 1024, 2048, 1024, 1024, 1, 64, 0.0, 1.0, 0.0, FAKE, None) == ESHAPE
+
+
+def test_stga_shot_workspace_and_argument_errors(lib):
+    w = lib.moga_stga_shot_workspace_bytes
+    assert w(372, 10, 3) >= 256 + 16 * (124 + 10)
+    assert w(0, 1, 3) == 0 and w(10, 0, 3) == 0 and w(10, 1, 0) == 0
+    s = lib.moga_stga_shot_attention
+    need = w(6, 2, 3)
+    args = lambda **kw: [kw.get("Q", FAKE), FAKE, FAKE, kw.get("T", 6), 30, 52, kw.get("ss", FAKE),  # noqa: E731
+                         kw.get("n", 2), 3, 30, kw.get("tw", 26), 1, 2, kw.get("D", 128), 0.0, 1.0, 0.0, FAKE,
+                         kw.get("ws", FAKE), kw.get("wsb", need), None]
+    assert s(*args(Q=None)) == ENULL
+    assert s(*args(ss=None)) == ENULL
+    assert s(*args(tw=25)) == ESHAPE            # 25 does not divide 52
+    assert s(*args(n=0)) == ESHAPE
+    assert s(*args(n=7)) == ESHAPE              # more shots than frames
+    assert s(*args(D=100)) == EUNSUP
+    assert s(*args(ws=None)) == EWS
+    assert s(*args(wsb=need - 1)) == EWS

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from parity import assert_gate_close, assert_output_close
-from workloads import get_workload, make_inputs, sample_rows
+from workloads import get_workload, make_inputs, make_shots, sample_rows
 from workloads.gen import to_numpy_f32
 
 pytestmark = pytest.mark.gpu
@@ -149,6 +149,29 @@ def test_stga(moga, T, Hs, Ws, win_t, th, tw, H, D, alpha, beta):
     assert_output_close(_np(out), ref, "STGA")
 
 
+@pytest.mark.parametrize("T,Hs,Ws,shots,win_t,th,tw,aug,H,D,alpha,beta", [
+    (7, 6, 10, [0, 3, 4, 7], 2, 3, 5, True, 2, 128, 1.0, 0.0),    # a one-frame shot, ragged windows
+    (9, 30, 52, [0, 5, 9], 3, 30, 26, True, 1, 128, 0.5, 0.5),    # Wan-like frames, 780-token tiles
+    (8, 8, 8, [0, 2, 3, 8], 3, 4, 8, False, 2, 64, 1.0, 1.0),     # no augmentation
+    (6, 4, 4, [0, 6], 2, 4, 4, True, 1, 64, 1.0, 0.0),            # one shot: plain windows
+    (5, 4, 8, [0, 1, 2, 3, 4, 5], 4, 2, 4, True, 2, 128, 1.0, 0.0),  # every frame its own shot
+])
+def test_stga_shot(moga, T, Hs, Ws, shots, win_t, th, tw, aug, H, D, alpha, beta):
+    N = T * Hs * Ws
+    print(f"[parity] stga-shot N={N} shots={shots} geo={win_t, th, tw} aug={aug} H={H} D={D}", flush=True)
+    inp = _inputs("tiny", N=N, H=H, D=D, M=2)
+    Q, K, V = inp["Q"], inp["K"], inp["V"]
+    O = V.clone() if beta != 0 else None
+    ss = torch.tensor(shots, dtype=torch.int32, device=DEV)
+    out = moga.moga_stga_shot_attention(Q, K, V, T, Hs, Ws, ss, win_t, th, tw, augment=aug, alpha=alpha,
+                                        beta=beta, O=O)
+    torch.cuda.synchronize()
+    ref = oracle.stga_shot_attention(_np(Q), _np(K), _np(V), T, Hs, Ws, shots, win_t, th, tw, 1 / math.sqrt(D),
+                                     aug)
+    ref = alpha * ref + beta * _np(V)
+    assert_output_close(_np(out), ref, "shot STGA")
+
+
 # ---------------------------------------------------------------------------
 # Full workload sizes, in the launch configuration the benchmark times
 # ---------------------------------------------------------------------------
@@ -182,6 +205,38 @@ def test_full_size_sampled(moga, name):
     got = _np(O[torch.from_numpy(rows).to(DEV)])
     e = assert_output_close(got, want, f"{name} sampled O")
     print(f"[parity] full {name}: {rows.size} rows, {e}", flush=True)
+
+
+def test_full_size_visual_block(moga):
+    """Minute-scale clip with a seeded multi-shot layout: the visual output
+    (MoGA + shot-aware STGA + per-frame attention) / 3 on sampled tokens,
+    including every shot's first and last frame."""
+    wl = get_workload("minute_372f")
+    s = dict(wl.stga)
+    shots = make_shots(s["T"], wl.seed)
+    s["shot_start"] = shots
+    print(f"[parity] visual block minute_372f shots={shots}", flush=True)
+    inp = make_inputs(wl, device=DEV)
+    X, Wr, Q, K, V = (inp[k] for k in ("X", "Wr", "Q", "K", "V"))
+    fwd = moga.MogaForward(wl.N, wl.d_model, wl.H, wl.D, wl.M, DEV, stga=s)
+    O = fwd(X, Wr, Q, K, V)
+    torch.cuda.synchronize()
+    Xn, Wn, Qn, Kn, Vn = _np(X), _np(Wr), _np(Q), _np(K), _np(V)
+    g_ref, gate_ref, _ = oracle.route(Xn, Wn)
+    np.testing.assert_array_equal(fwd.group_id.cpu().numpy(), g_ref)
+    rows = sample_rows(g_ref, wl.M, per_group=2, seed=wl.seed)
+    area = s["Hs"] * s["Ws"]
+    edge = [f * area + o for t in shots[1:-1] for f in (t - 1, t) for o in (0, area - 1)]
+    rows = np.unique(np.concatenate([rows, np.asarray(edge, dtype=np.int64)]))
+    scale = 1 / math.sqrt(wl.D)
+    want = oracle.moga_output_rows(Xn, Wn, Qn, Kn, Vn, wl.M, rows, routed=(g_ref, gate_ref))
+    want = want + oracle.stga_shot_attention_rows(Qn, Kn, Vn, s["T"], s["Hs"], s["Ws"], shots, s["win_t"],
+                                                  s["tile_h"], s["tile_w"], scale, rows)
+    frame_ids = oracle.stga_group_ids(s["T"], s["Hs"], s["Ws"], 1, s["Hs"], s["Ws"])
+    want = (want + oracle.stga_attention_rows(Qn, Kn, Vn, frame_ids, scale, rows)) / 3.0
+    got = _np(O[torch.from_numpy(rows).to(DEV)])
+    e = assert_output_close(got, want, "minute_372f visual block sampled O")
+    print(f"[parity] visual block: {rows.size} rows, {e}", flush=True)
 
 
 @pytest.mark.parametrize("late,label", [(2.0, "overflow-fallback"), (0.9, "fixed-offset")])
