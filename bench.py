@@ -1,17 +1,21 @@
 """Benchmark of the MoGA forward hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--path P] [--no-cpu-baseline]
 
 A step is one pass of the whole path over one synthetic batch already resident
-in HBM: route -> permute (sort + Q/K/V gather) -> group attention with the
-gated unpermute fused in (-> STGA sum for workloads that have it).  Prints ONE
-JSON line.
+in HBM: route -> permute -> gated group attention (-> STGA sum for workloads
+that have it).  --path picks how attention meets the permutation (default
+fused_epilogue: sort + Q/K/V gather, attention with the gated unpermute in
+its epilogue; gather_on_load: sort only, attention reads Q/K/V rows through
+perm and writes the gated output in place; separate: gather, attention,
+unpermute).
+Prints ONE JSON line.
 
 value = effective TFLOP/s of the whole step, counting only within-group
 attention FLOPs 4*H*D*sum_g n_g^2 (plus the STGA windows when present);
 tokens_per_s = N / step time.  The roofline object covers the dominant kernel
-(group attention with the gated unpermute fused in), timed live with HIP
-events on the stream it runs on.
+(the gated group attention), timed live with HIP events on the stream it runs
+on.
 """
 
 from __future__ import annotations
@@ -40,6 +44,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None)
+    ap.add_argument("--path", default="fused_epilogue", choices=["fused_epilogue", "gather_on_load", "separate"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2000, help="sampled query rows per group for the oracle")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -69,13 +74,16 @@ def source_hash(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_entry(launch_flops_key):
+def traffic_entry(kernel, workload):
     """HBM bytes per attention launch from the committed counter summary, or
-    None when the kernel source changed after the counters were taken."""
+    None when it covers another kernel or workload, or the kernel source
+    changed after the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
+        return None
+    if t.get("kernel") != kernel or t.get("workload") != workload:
         return None
     if t.get("attention_source_sha256_16") != source_hash(ATTN_SOURCE):
         return None
@@ -143,23 +151,37 @@ def main():
     torch.cuda.set_device(dev)
     inp = make_inputs(wl, device=dev)
     X, Wr, Q, K, V = (inp[k] for k in ("X", "Wr", "Q", "K", "V"))
-    fwd = moga.MogaForward(wl.N, wl.d_model, wl.H, wl.D, wl.M, dev, stga=wl.stga)
+    fwd = moga.MogaForward(wl.N, wl.d_model, wl.H, wl.D, wl.M, dev, stga=wl.stga, path=args.path)
     stream = torch.cuda.current_stream()
+    attn_kernel = {"gather_on_load": "attn_kernel (moga_group_attention_fused)",
+                   "fused_epilogue": "attn_kernel (moga_group_attention_unpermute)",
+                   "separate": "attn_kernel (moga_group_attention) + unpermute_kernel"}[args.path]
 
     def step(ev=None):
-        # the library calls of MogaForward.__call__ (fused attention + unpermute),
-        # with HIP events on the same stream between stages
+        # the library calls of MogaForward.__call__ for the chosen path, with
+        # HIP events on the same stream between stages
         if ev is not None:
             ev[0].record(stream)
         moga.moga_route(X, Wr, None, fwd.group_id, fwd.gate)
         if ev is not None:
             ev[1].record(stream)
-        moga.moga_permute(fwd.group_id, wl.M, Q, K, V, fwd.Qp, fwd.Kp, fwd.Vp, fwd.perm, fwd.cu_seqlens,
-                          fwd.max_seqlen, fwd.ws_perm)
+        if args.path == "gather_on_load":
+            moga.moga_permute(fwd.group_id, wl.M, perm=fwd.perm, cu_seqlens=fwd.cu_seqlens,
+                              max_seqlen=fwd.max_seqlen, ws=fwd.ws_perm)
+        else:
+            moga.moga_permute(fwd.group_id, wl.M, Q, K, V, fwd.Qp, fwd.Kp, fwd.Vp, fwd.perm, fwd.cu_seqlens,
+                              fwd.max_seqlen, fwd.ws_perm)
         if ev is not None:
             ev[2].record(stream)
-        moga.moga_group_attention_unpermute(fwd.Qp, fwd.Kp, fwd.Vp, fwd.cu_seqlens, fwd.perm, fwd.gate, 0.0, 0.0,
-                                            fwd.O, fwd.ws_attn)
+        if args.path == "gather_on_load":
+            moga.moga_group_attention_fused(Q, K, V, fwd.cu_seqlens, fwd.perm, fwd.gate, 0.0, 0.0, fwd.O,
+                                            fwd.ws_attn)
+        elif args.path == "fused_epilogue":
+            moga.moga_group_attention_unpermute(fwd.Qp, fwd.Kp, fwd.Vp, fwd.cu_seqlens, fwd.perm, fwd.gate, 0.0,
+                                                0.0, fwd.O, fwd.ws_attn)
+        else:
+            moga.moga_group_attention(fwd.Qp, fwd.Kp, fwd.Vp, fwd.cu_seqlens, 0.0, fwd.Op, fwd.ws_attn)
+            moga.moga_unpermute(fwd.Op, fwd.perm, fwd.gate, 0.0, fwd.O)
         if ev is not None:
             ev[3].record(stream)
         if wl.stga is not None:
@@ -182,7 +204,7 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
-    stages = ["route", "permute", "group_attention_unpermute", "stga"]
+    stages = ["route", "permute", "group_attention", "stga"]
     breakdown = {s: sum(e[k].elapsed_time(e[k + 1]) for e in evs) / args.steps for k, s in enumerate(stages)}
     if wl.stga is None:
         breakdown.pop("stga")
@@ -196,13 +218,13 @@ def main():
         flops_stga = 4.0 * wl.H * wl.D * gsize * gsize * (wl.N // gsize)
     step_flops = flops_moga + flops_stga
     value = step_flops / (ms_per_step * 1e-3) / 1e12
-    attn_ms = breakdown["group_attention_unpermute"]
+    attn_ms = breakdown["group_attention"]
     achieved = flops_moga / (attn_ms * 1e-3) / 1e12
 
-    traffic = traffic_entry(None)
+    traffic = traffic_entry(attn_kernel, wl.name)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "kernel": "attn_kernel (moga_group_attention_unpermute)", "launch_ms": round(attn_ms, 4),
+                "kernel": attn_kernel, "launch_ms": round(attn_ms, 4),
                 "flops_per_launch": flops_moga}
     mean = wl.N / wl.M
     out = {
@@ -218,7 +240,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded Gaussian-mixture tokens, random-init router and Q/K/V projections)",
-        "config": {"workload": wl.name, "N": wl.N, "d_model": wl.d_model, "H": wl.H, "D": wl.D, "M": wl.M,
+        "config": {"workload": wl.name, "path": args.path, "N": wl.N, "d_model": wl.d_model, "H": wl.H, "D": wl.D, "M": wl.M,
                    "group_max_over_mean": round(max(counts) / mean, 3),
                    "skew_sum_n2_over_uniform": round(sum(c * c for c in counts) / (wl.N * mean), 3),
                    "stga": wl.stga},
@@ -228,10 +250,9 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
-    hbm = {  # algorithmic bytes per launch of the HBM-bound stages
-        "route": wl.N * (2 * wl.d_model + 8) + 2 * wl.M * wl.d_model,
-        "permute": wl.N * (12 * wl.H * wl.D + 16),
-    }
+    hbm = {"route": wl.N * (2 * wl.d_model + 8) + 2 * wl.M * wl.d_model}  # algorithmic bytes per launch
+    if args.path != "gather_on_load":  # sort + gather; the sort alone is latency-bound (reported in ms only)
+        hbm["permute"] = wl.N * (12 * wl.H * wl.D + 16)
     out["hbm_gbs"] = {k: round(b / (breakdown[k] * 1e-3) / 1e9, 1) for k, b in hbm.items()}
     out["hbm_frac"] = {k: round(v / PEAK_HBM_GBS, 4) for k, v in out["hbm_gbs"].items()}
     if not args.no_cpu_baseline:

@@ -125,6 +125,22 @@ int moga_group_attention_unpermute(const void* Qp, const void* Kp, const void* V
                                    float beta, void* O, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moga_group_attention_fused -- the gated group attention read in place
+ *   (gather on load; MoGA output equation, Algorithm 1 steps 2 to 4 after the
+ *   sort): Q, K, V are the ORIGINAL-order tensors bf16 [N, H, D], and
+ *   permuted row j of a group is read from token perm[j], so no gathered
+ *   copies are needed (moga_permute may be called with Q = K = V = NULL).
+ *   O[n] = beta * O[n] + gate[n] * Attn(n) for every token n.
+ *   cu_seqlens, perm as produced by moga_permute; gate float32 [N]; ws as for
+ *   MOGA_OP_GROUP_ATTENTION.  beta = 0 does not read O.  O must not alias
+ *   Q, K or V.
+ */
+int moga_group_attention_fused(const void* Q, const void* K, const void* V,
+                               const int32_t* cu_seqlens, const int32_t* perm, const float* gate,
+                               int64_t N, int32_t H, int32_t D, int32_t M, float softmax_scale,
+                               float beta, void* O, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * moga_unpermute -- gate and return rows to original order
  *   (MoGA output equation in "Grouped Attention"; Algorithm 1 step 4):
  *   O[perm[j]] = beta * O[perm[j]] + gate[perm[j]] * Op[j]  (float32 math).
@@ -161,14 +177,16 @@ int moga_stga_attention(const void* Q, const void* K, const void* V,
  *   into windows of win_t frames, the last one shorter if the shot length is
  *   not a multiple of win_t.  The queries of a window are its frames' tokens
  *   inside one tile_h x tile_w spatial tile; its keys and values are those
- *   tokens, plus (augment != 0) the same tile of the previous shot's last
- *   frame for the shot's first window and of the next shot's first frame for
- *   the shot's last window.  O[n] = beta * O[n] + alpha * STGA(n).
+ *   tokens, plus the same tile of the previous shot's last `augment` frames
+ *   for the shot's first window and of the next shot's first `augment`
+ *   frames for the shot's last window (clipped to those shots; augment = 0
+ *   turns augmentation off, 0 <= augment <= 64).
+ *   O[n] = beta * O[n] + alpha * STGA(n).
  *   shot_start: DEVICE int32 [n_shots + 1], 0 = shot_start[0] < ... <
  *   shot_start[n_shots] = T (not checked on the host; boundaries outside
  *   that order give unspecified output for the affected frames, never an
  *   out-of-bounds access).  tile_h, tile_w must divide Hs, Ws and
- *   (win_t + 2) * tile_h * tile_w must be at most 2^20.
+ *   (win_t + 2 * augment) * tile_h * tile_w must be at most 2^20.
  *   ws: device workspace of moga_stga_shot_workspace_bytes(T, n_shots, win_t)
  *   bytes (the window table, rebuilt on every call).
  */

@@ -30,8 +30,8 @@ Readings of points the pages leave open (each is listed in the design doc):
     frame-major tokens n = (t * Hs + y) * Ws + x, with no gate;
   * shot-aware STGA: windows restart at every shot start; the keys and values
     (never the queries) of a shot's first window also hold the previous
-    shot's last frame, those of its last window the next shot's first frame,
-    each restricted to the same spatial tile (shot_windows);
+    shot's last frame(s), those of its last window the next shot's first
+    frame(s), each restricted to the same spatial tile (shot_windows);
   * the visual output is the plain mean of MoGA, shot-aware STGA and
     per-frame attention.
 """
@@ -274,7 +274,7 @@ def stga_attention(Q, K, V, T, Hs, Ws, win_t, tile_h, tile_w, scale,
 # Shot-aware STGA, per-frame attention and the visual block (STGA section)
 # ---------------------------------------------------------------------------
 
-def shot_windows(shot_start, win_t, aug=True):
+def shot_windows(shot_start, win_t, aug=1):
     """Temporal windows of the shot-aware STGA.
 
     STGA section: frames are grouped along time and frames of different shots
@@ -282,10 +282,14 @@ def shot_windows(shot_start, win_t, aug=True):
     augmented with latent frames from the adjacent shots.  Reading used: each
     shot [a_s, a_{s+1}) is cut into consecutive windows of win_t frames (the
     last one may be shorter); the first window of a shot (other than the first
-    shot) also takes the previous shot's last frame as keys, and the last
-    window of a shot (other than the last shot) the next shot's first frame.
-    Returns a list of (t0, nt, prev_frame or -1, next_frame or -1).
+    shot) also takes the last ``aug`` frames of the previous shot as keys, and
+    the last window of a shot (other than the last shot) the first ``aug``
+    frames of the next shot, each clipped to that shot's length.  aug = 1
+    gives two augmentation frames for a shot held in one window (one from
+    each side); aug = 0 (or False) turns augmentation off.
+    Returns a list of (t0, nt, prev_frames, next_frames).
     """
+    aug = int(aug)
     a = [int(x) for x in shot_start]
     out = []
     for sh in range(len(a) - 1):
@@ -293,13 +297,13 @@ def shot_windows(shot_start, win_t, aug=True):
         starts = list(range(lo, hi, win_t))
         for k, t0 in enumerate(starts):
             nt = min(win_t, hi - t0)
-            prev = lo - 1 if (aug and k == 0 and sh > 0) else -1
-            nxt = hi if (aug and k == len(starts) - 1 and sh < len(a) - 2) else -1
+            prev = list(range(max(a[sh - 1], lo - aug), lo)) if (k == 0 and sh > 0) else []
+            nxt = list(range(hi, min(a[sh + 2], hi + aug))) if (k == len(starts) - 1 and sh < len(a) - 2) else []
             out.append((t0, nt, prev, nxt))
     return out
 
 
-def stga_shot_attention(Q, K, V, T, Hs, Ws, shot_start, win_t, tile_h, tile_w, scale, aug=True):
+def stga_shot_attention(Q, K, V, T, Hs, Ws, shot_start, win_t, tile_h, tile_w, scale, aug=1):
     """Shot-aware STGA over frame-major tokens (float64 [N, H, D]): for each
     window and spatial tile, the window's tokens in the tile attend to those
     same tokens plus, as extra keys, the tile's tokens in the augmentation
@@ -311,7 +315,7 @@ def stga_shot_attention(Q, K, V, T, Hs, Ws, shot_start, win_t, tile_h, tile_w, s
                          for y in range(y0, y0 + tile_h) for x in range(x0, x0 + tile_w)], dtype=np.int64)
     out = np.zeros(Q.shape, dtype=np.float64)
     for t0, nt, prev, nxt in shot_windows(shot_start, win_t, aug):
-        extra = [f for f in (prev, nxt) if f >= 0]
+        extra = prev + nxt
         for y0 in range(0, Hs, tile_h):
             for x0 in range(0, Ws, tile_w):
                 q_tok = tokens(range(t0, t0 + nt), y0, x0)
@@ -324,7 +328,7 @@ def stga_shot_attention(Q, K, V, T, Hs, Ws, shot_start, win_t, tile_h, tile_w, s
     return out
 
 
-def stga_shot_attention_rows(Q, K, V, T, Hs, Ws, shot_start, win_t, tile_h, tile_w, scale, rows, aug=True):
+def stga_shot_attention_rows(Q, K, V, T, Hs, Ws, shot_start, win_t, tile_h, tile_w, scale, rows, aug=1):
     """Shot-aware STGA output of selected tokens only (float64 [len(rows), H, D]);
     the same windows and key sets as stga_shot_attention."""
     area = tile_h * tile_w
@@ -338,7 +342,7 @@ def stga_shot_attention_rows(Q, K, V, T, Hs, Ws, shot_start, win_t, tile_h, tile
         t, y, x = int(n) // (Hs * Ws), (int(n) // Ws) % Hs, int(n) % Ws
         t0, nt, prev, nxt = frame_win[t]
         y0, x0 = y // tile_h * tile_h, x // tile_w * tile_w
-        frames = list(range(t0, t0 + nt)) + [f for f in (prev, nxt) if f >= 0]
+        frames = list(range(t0, t0 + nt)) + prev + nxt
         k_tok = np.array([(f * Hs + yy) * Ws + xx for f in frames
                           for yy in range(y0, y0 + tile_h) for xx in range(x0, x0 + tile_w)], dtype=np.int64)
         assert k_tok.size == len(frames) * area
@@ -353,7 +357,7 @@ def frame_attention(Q, K, V, T, Hs, Ws, scale):
     return stga_attention(Q, K, V, T, Hs, Ws, 1, Hs, Ws, scale)
 
 
-def visual_block_forward(X, Wr, Q, K, V, M, T, Hs, Ws, shot_start, win_t, tile_h, tile_w, scale=None, aug=True):
+def visual_block_forward(X, Wr, Q, K, V, M, T, Hs, Ws, shot_start, win_t, tile_h, tile_w, scale=None, aug=1):
     """Visual attention output of the STGA section: the arithmetic mean of the
     MoGA, shot-aware STGA and per-frame attention outputs (float64)."""
     D = Q.shape[2]

@@ -135,6 +135,33 @@ def moga_group_attention_unpermute(Qp, Kp, Vp, cu_seqlens, perm, gate, softmax_s
     return O
 
 
+def moga_group_attention_fused(Q, K, V, cu_seqlens, perm, gate, softmax_scale=0.0, beta=0.0, O=None, ws=None):
+    """Gated group attention on the original-order Q/K/V (rows read through
+    perm): O[n] = beta*O[n] + gate[n]*Attn(n)."""
+    _need(Q, "Q", BF16, 3)
+    N, H, D = Q.shape
+    _need(K, "K", BF16, 3, Q.shape)
+    _need(V, "V", BF16, 3, Q.shape)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _need(perm, "perm", torch.int32, 1, (N,))
+    _need(gate, "gate", torch.float32, 1, (N,))
+    M = cu_seqlens.shape[0] - 1
+    if O is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs an existing O")
+        O = torch.empty_like(Q)
+    _need(O, "O", BF16, 3, Q.shape)
+    for name, t in (("Q", Q), ("K", K), ("V", V)):
+        if O.data_ptr() == t.data_ptr():
+            raise ValueError(f"O must not alias {name}")
+    ws, nbytes = _workspace(MOGA_OP_GROUP_ATTENTION, N, M, H, D, ws, Q.device)
+    check(_lib.LIB.moga_group_attention_fused(ptr(Q), ptr(K), ptr(V), ptr(cu_seqlens), ptr(perm), ptr(gate), N, H, D,
+                                              M, float(softmax_scale), float(beta), ptr(O), ptr(ws), nbytes,
+                                              stream_handle()),
+          "moga_group_attention_fused")
+    return O
+
+
 def moga_unpermute(Op, perm, gate, beta=0.0, O=None):
     """O[perm[j]] = beta * O[perm[j]] + gate[perm[j]] * Op[j]."""
     _need(Op, "Op", BF16, 3)
@@ -175,10 +202,11 @@ def moga_stga_shot_workspace_bytes(T: int, n_shots: int, win_t: int) -> int:
     return int(_lib.LIB.moga_stga_shot_workspace_bytes(T, n_shots, win_t))
 
 
-def moga_stga_shot_attention(Q, K, V, T, Hs, Ws, shot_start, win_t, tile_h, tile_w, augment=True,
+def moga_stga_shot_attention(Q, K, V, T, Hs, Ws, shot_start, win_t, tile_h, tile_w, augment=1,
                              softmax_scale=0.0, alpha=1.0, beta=0.0, O=None, ws=None):
     """Shot-aware window attention over frame-major tokens; O = beta*O + alpha*STGA.
-    shot_start: int32 GPU tensor [n_shots + 1] (0, ..., T)."""
+    shot_start: int32 GPU tensor [n_shots + 1] (0, ..., T); augment: frames
+    taken from each adjacent shot as extra keys (0: none; True counts as 1)."""
     _need(Q, "Q", BF16, 3)
     N, H, D = Q.shape
     _need(K, "K", BF16, 3, Q.shape)
@@ -199,7 +227,7 @@ def moga_stga_shot_attention(Q, K, V, T, Hs, Ws, shot_start, win_t, tile_h, tile
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=Q.device)
     _need(ws, "ws")
     check(_lib.LIB.moga_stga_shot_attention(ptr(Q), ptr(K), ptr(V), T, Hs, Ws, ptr(shot_start), n_shots, win_t,
-                                            tile_h, tile_w, int(bool(augment)), H, D, float(softmax_scale),
+                                            tile_h, tile_w, int(augment), H, D, float(softmax_scale),
                                             float(alpha), float(beta), ptr(O), ptr(ws),
                                             ws.numel() * ws.element_size(), stream_handle()),
           "moga_stga_shot_attention")
@@ -223,27 +251,40 @@ def moga_balance_stats(group_id, gate, M, alpha=0.1, ws=None):
 
 
 class MogaForward:
-    """Preallocated buffers for one MoGA layer pass (route, permute, group
-    attention and gated unpermute -- fused into one kernel unless
-    ``fused=False`` -- and, when ``stga`` geometry is given, the STGA branch).
-    ``__call__`` launches the library calls back to back on the current
-    stream and allocates nothing.
+    """Preallocated buffers for one MoGA layer pass and, when ``stga``
+    geometry is given, the STGA branch.  ``__call__`` launches the library
+    calls back to back on the current stream and allocates nothing.
+
+    ``path`` selects how the group attention meets the permutation:
+      "fused_epilogue" (default): gathered Q/K/V copies, attention with the
+        gated unpermute in its epilogue (moga_group_attention_unpermute);
+      "gather_on_load": sort only, then moga_group_attention_fused reads
+        Q/K/V rows through perm -- no gathered copies (3*N*H*D bf16 less
+        device memory) at about the same step time (the gather pass saved is
+        spent again on indirect row reads inside the attention);
+      "separate": gathered copies, moga_group_attention, moga_unpermute.
 
     ``stga``: dict with T, Hs, Ws, win_t, tile_h, tile_w and optionally
-    ``shot_start`` (a list of shot start frames ending with T) and ``augment``.
-    Without shots the branch is the plain static-window STGA, added with
-    ``stga_weight``.  With ``shot_start`` the pass computes the visual
-    attention output of the STGA section: the mean of MoGA, shot-aware STGA
-    and per-frame attention."""
+    ``shot_start`` (a list of shot start frames ending with T) and ``augment``
+    (frames per adjacent shot, default 1).  Without shots the branch is the
+    plain static-window STGA, added with ``stga_weight``.  With
+    ``shot_start`` the pass computes the visual attention output of the STGA
+    section: the mean of MoGA, shot-aware STGA and per-frame attention."""
 
-    def __init__(self, N, d_model, H, D, M, device, stga=None, fused=True):
+    PATHS = ("fused_epilogue", "gather_on_load", "separate")
+
+    def __init__(self, N, d_model, H, D, M, device, stga=None, path="fused_epilogue"):
+        if path not in self.PATHS:
+            raise ValueError(f"path must be one of {self.PATHS}")
         self.N, self.d_model, self.H, self.D, self.M, self.stga = N, d_model, H, D, M, stga
-        self.fused = fused
+        self.path = path
         e = lambda *s, dt=BF16: torch.empty(*s, dtype=dt, device=device)  # noqa: E731
         self.group_id = e(N, dt=torch.int32)
         self.gate = e(N, dt=torch.float32)
-        self.Qp, self.Kp, self.Vp, self.O = (e(N, H, D) for _ in range(4))
-        self.Op = None if fused else e(N, H, D)
+        self.O = e(N, H, D)
+        copies = path != "gather_on_load"
+        self.Qp, self.Kp, self.Vp = (e(N, H, D) if copies else None for _ in range(3))
+        self.Op = e(N, H, D) if path == "separate" else None
         self.perm = e(N, dt=torch.int32)
         self.cu_seqlens = e(M + 1, dt=torch.int32)
         self.max_seqlen = e(1, dt=torch.int32)
@@ -260,12 +301,18 @@ class MogaForward:
         """O = moga_weight * MoGA + stga_weight * STGA (the STGA term only with
         geometry); with shots, O = (MoGA + shot STGA + per-frame) / 3."""
         moga_route(X, Wr, bias, self.group_id, self.gate)
-        moga_permute(self.group_id, self.M, Q, K, V, self.Qp, self.Kp, self.Vp, self.perm, self.cu_seqlens,
-                     self.max_seqlen, self.ws_perm)
-        if self.fused:
+        if self.path == "gather_on_load":
+            moga_permute(self.group_id, self.M, perm=self.perm, cu_seqlens=self.cu_seqlens,
+                         max_seqlen=self.max_seqlen, ws=self.ws_perm)
+            moga_group_attention_fused(Q, K, V, self.cu_seqlens, self.perm, self.gate, softmax_scale, 0.0, self.O,
+                                       self.ws_attn)
+        else:
+            moga_permute(self.group_id, self.M, Q, K, V, self.Qp, self.Kp, self.Vp, self.perm, self.cu_seqlens,
+                         self.max_seqlen, self.ws_perm)
+        if self.path == "fused_epilogue":
             moga_group_attention_unpermute(self.Qp, self.Kp, self.Vp, self.cu_seqlens, self.perm, self.gate,
                                            softmax_scale, 0.0, self.O, self.ws_attn)
-        else:
+        elif self.path == "separate":
             moga_group_attention(self.Qp, self.Kp, self.Vp, self.cu_seqlens, softmax_scale, self.Op, self.ws_attn)
             moga_unpermute(self.Op, self.perm, self.gate, 0.0, self.O)
         g = self.stga
@@ -276,7 +323,7 @@ class MogaForward:
             third = 1.0 / 3.0
             # O = MoGA  ->  (MoGA + shot STGA) / 3  ->  + per-frame / 3
             moga_stga_shot_attention(Q, K, V, g["T"], g["Hs"], g["Ws"], self.shot_start, g["win_t"], g["tile_h"],
-                                     g["tile_w"], g.get("augment", True), softmax_scale, third, third, self.O,
+                                     g["tile_w"], g.get("augment", 1), softmax_scale, third, third, self.O,
                                      self.ws_shot)
             moga_stga_attention(Q, K, V, g["T"], g["Hs"], g["Ws"], 1, g["Hs"], g["Ws"], softmax_scale, third, 1.0,
                                 self.O)

@@ -57,11 +57,12 @@ struct Work {
   int head;
   int64_t row0; // MoGA: first permuted row of the group
   int t0, y0, x0;  // STGA: window origin
-  int nt, e0, e1;  // shot-aware STGA: window frames, extra key frames (-1: none)
+  int nt, npre, pre_off, nxt_off;  // shot-aware STGA: window frames, frames before, frame offsets
 };
 
 // Learned groups: rows of group g are cu[g] .. cu[g+1]-1 of the permuted tensors.
 struct MogaRows {
+  static constexpr bool kIndirect = false;
   const int32_t* cu;
   const AttnSchedule* sched;
   int M, H;
@@ -86,8 +87,21 @@ struct MogaRows {
   __device__ __forceinline__ int64_t key(const Work& w, int i) const { return w.row0 + i; }
 };
 
+// Learned groups read in place (gather on load): permuted row j of a group is
+// original token perm[j], so Q, K and V are the unpermuted tensors and no
+// gathered copies exist.  Key rows are fetched a tile ahead (kIndirect).
+struct MogaPermRows {
+  static constexpr bool kIndirect = true;
+  MogaRows base;
+  const int32_t* perm;
+  __device__ __forceinline__ bool decode(int item, Work& w) const { return base.decode(item, w); }
+  __device__ __forceinline__ int64_t row(const Work& w, int i) const { return perm[w.row0 + i]; }
+  __device__ __forceinline__ int32_t key_index(const Work& w, int i) const { return perm[w.row0 + i]; }
+};
+
 // Static windows over frame-major tokens n = (t*Hs + y)*Ws + x.
 struct StgaRows {
+  static constexpr bool kIndirect = false;
   int Hs, Ws, win_t, tile_h, tile_w, nty, ntx, tiles_per_group, H, items;
   __device__ __forceinline__ bool decode(int item, Work& w) const {
     if (item >= items) return false;
@@ -119,10 +133,11 @@ struct StgaRows {
 };
 
 // One temporal window of the shot-aware STGA: frames t0 .. t0+nt-1 of one
-// shot, plus the frames prev / next of the neighbouring shots (-1: none)
-// whose tokens join the keys and values only.
+// shot, plus frames pre0 .. pre0+npre-1 of the previous shot and
+// nxt0 .. nxt0+nnxt-1 of the next one, whose tokens join the keys and values
+// only.
 struct ShotWindow {
-  int t0, nt, prev, next;
+  int t0, nt, pre0, npre, nxt0, nnxt;
 };
 
 // Shot-aware windows: queries are the window's own frames inside one spatial
@@ -130,6 +145,7 @@ struct ShotWindow {
 // Items: window-major, then spatial tile, head and query tile, so the query
 // tiles sharing one key set are consecutive (and land on one XCD).
 struct ShotRows {
+  static constexpr bool kIndirect = false;
   const ShotWindow* win;
   const int* nwin;
   int Hs, Ws, tile_h, tile_w, ntx, nspatial, tpg, H;
@@ -146,10 +162,12 @@ struct ShotRows {
     const int area = tile_h * tile_w;
     w.nq = sw.nt * area;
     if (w.q0 >= w.nq) return false;
+    // key frame tt: t0 + tt inside the window, then pre0 + (tt - nt), then nxt0 + (tt - nt - npre)
     w.nt = sw.nt;
-    w.e0 = sw.prev >= 0 ? sw.prev : sw.next;
-    w.e1 = sw.prev >= 0 ? sw.next : -1;
-    w.len = (sw.nt + (w.e0 >= 0) + (w.e1 >= 0)) * area;
+    w.npre = sw.nt + sw.npre;
+    w.pre_off = sw.pre0 - sw.nt;
+    w.nxt_off = sw.nxt0 - w.npre;
+    w.len = (sw.nt + sw.npre + sw.nnxt) * area;
     w.t0 = sw.t0;
     const int ty = sp / ntx;
     w.y0 = ty * tile_h;
@@ -170,7 +188,9 @@ struct ShotRows {
   __device__ __forceinline__ int64_t key(const Work& w, int i) const {
     const int area = tile_h * tile_w;
     const int tt = i / area;
-    const int frame = tt < w.nt ? w.t0 + tt : (tt == w.nt ? w.e0 : w.e1);
+    const int t0 = w.t0, pre_off = w.pre_off, nxt_off = w.nxt_off;  // values, not a select of field addresses
+    const int off = tt < w.npre ? pre_off : nxt_off;
+    const int frame = tt + (tt < w.nt ? t0 : off);
     return at(w, frame, i - tt * area);
   }
 };
@@ -222,6 +242,43 @@ __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ K, const
     key = key < w.len ? key : w.len - 1;
     const int64_t base = rows.key(w, key) * row_stride + hoff;
     const int lds_off = (wave * LOADS + j) * kWave * 8;  // uint16 elements, wave-uniform
+    __builtin_amdgcn_global_load_lds((global_void*)(K + base + (p ^ kswz(r, CPR)) * 8), (lds_void*)(Ks + lds_off),
+                                     16, 0, 0);
+    __builtin_amdgcn_global_load_lds((global_void*)(V + base + (p ^ vswz(r, CPR)) * 8), (lds_void*)(Vs + lds_off),
+                                     16, 0, 0);
+  }
+}
+
+// Gather-on-load variant of issue_tile: the token row of every chunk this
+// lane loads was fetched beforehand (fetch_keys) into kidx.
+template <int D, int NW>
+constexpr int tile_loads() { return kBN * (D / 8) / (NW * kWave); }
+
+template <int D, int NW, class Rows>
+__device__ __forceinline__ void fetch_keys(const Rows& rows, const Work& w, int k0, int wave, int lane,
+                                           int32_t (&kidx)[tile_loads<D, NW>()]) {
+  constexpr int CPR = D / 8;
+#pragma unroll
+  for (int j = 0; j < tile_loads<D, NW>(); ++j) {
+    const int r = ((wave * tile_loads<D, NW>() + j) * kWave + lane) / CPR;
+    int key = k0 + r;
+    key = key < w.len ? key : w.len - 1;
+    kidx[j] = rows.key_index(w, key);
+  }
+}
+
+template <int D, int NW>
+__device__ __forceinline__ void issue_tile_idx(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                                               uint16_t* Ks, uint16_t* Vs, const int32_t (&kidx)[tile_loads<D, NW>()],
+                                               int64_t row_stride, int64_t hoff, int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int LOADS = tile_loads<D, NW>();
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) {
+    const int q = (wave * LOADS + j) * kWave + lane;
+    const int r = q / CPR, p = q % CPR;
+    const int64_t base = (int64_t)kidx[j] * row_stride + hoff;
+    const int lds_off = (wave * LOADS + j) * kWave * 8;
     __builtin_amdgcn_global_load_lds((global_void*)(K + base + (p ^ kswz(r, CPR)) * 8), (lds_void*)(Ks + lds_off),
                                      16, 0, 0);
     __builtin_amdgcn_global_load_lds((global_void*)(V + base + (p ^ vswz(r, CPR)) * 8), (lds_void*)(Vs + lds_off),
@@ -359,7 +416,9 @@ __device__ __forceinline__ void tile_max(const uint16_t* Ks, int k0, int len, co
 //   kEpiScaled: O[row] = alpha * attn + beta * O[row]          (STGA)
 //   kEpiGated:  n = perm[row]; O[n] = gate[n] * attn + beta * O[n]
 //               (the gated unpermute fused into the attention)
-enum { kEpiPlain = 0, kEpiScaled = 1, kEpiGated = 2 };
+//   kEpiGatedInPlace: the row already is the original token n (gather on
+//               load); O[n] = gate[n] * attn + beta * O[n]
+enum { kEpiPlain = 0, kEpiScaled = 1, kEpiGated = 2, kEpiGatedInPlace = 3 };
 struct Epilogue {
   float alpha, beta;
   const int32_t* perm;
@@ -387,7 +446,18 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave) void attn_kernel(
   const int nfull = w.len / kBN;            // tiles without a group end inside
   const int ntiles = (w.len + kBN - 1) / kBN;
 
-  issue_tile<D, NW>(K, V, Ks0, Vs0, rows, w, row_stride, hoff, 0, wave, lane);
+  // Tile t's K/V loads; with gather on load, also fetch tile t+1's key rows.
+  [[maybe_unused]] int32_t kidx[tile_loads<D, NW>()];
+  auto issue = [&](uint16_t* Kd, uint16_t* Vd, int t) {
+    if constexpr (Rows::kIndirect) {
+      issue_tile_idx<D, NW>(K, V, Kd, Vd, kidx, row_stride, hoff, wave, lane);
+      if (t + 1 < ntiles) fetch_keys<D, NW>(rows, w, (t + 1) * kBN, wave, lane, kidx);
+    } else {
+      issue_tile<D, NW>(K, V, Kd, Vd, rows, w, row_stride, hoff, t * kBN, wave, lane);
+    }
+  };
+  if constexpr (Rows::kIndirect) fetch_keys<D, NW>(rows, w, 0, wave, lane, kidx);
+  issue(Ks0, Vs0, 0);
 
   // this lane's two queries (blocks b = 0, 1) and their Q fragments
   int64_t qrow[QB];
@@ -419,7 +489,7 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave) void attn_kernel(
   auto begin_tile = [&](uint16_t* Kn, uint16_t* Vn, int t) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 1 < ntiles) issue_tile<D, NW>(K, V, Kn, Vn, rows, w, row_stride, hoff, (t + 1) * kBN, wave, lane);
+    if (t + 1 < ntiles) issue(Kn, Vn, t + 1);
   };
   // kMax: row maxima only (into mx) instead of softmax and P V
   auto run = [&](auto max_only) {
@@ -466,10 +536,12 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave) void attn_kernel(
   // with the exact maxima, where no score exceeds its offset).
   if (__syncthreads_or(over)) {
     __syncthreads();
-    issue_tile<D, NW>(K, V, Ks0, Vs0, rows, w, row_stride, hoff, 0, wave, lane);
+    if constexpr (Rows::kIndirect) fetch_keys<D, NW>(rows, w, 0, wave, lane, kidx);
+    issue(Ks0, Vs0, 0);
     run(std::true_type{});
     __syncthreads();
-    issue_tile<D, NW>(K, V, Ks0, Vs0, rows, w, row_stride, hoff, 0, wave, lane);
+    if constexpr (Rows::kIndirect) fetch_keys<D, NW>(rows, w, 0, wave, lane, kidx);
+    issue(Ks0, Vs0, 0);
 #pragma unroll
     for (int b = 0; b < QB; ++b)
 #pragma unroll
@@ -489,6 +561,9 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave) void attn_kernel(
       keep = epi.beta;
     } else if constexpr (kEpi == kEpiGated) {
       orow = epi.perm[qrow[b]];
+      scale *= epi.gate[orow];
+      keep = epi.beta;
+    } else if constexpr (kEpi == kEpiGatedInPlace) {
       scale *= epi.gate[orow];
       keep = epi.beta;
     }
@@ -546,9 +621,10 @@ __global__ __launch_bounds__(kWave) void schedule_kernel(const int32_t* __restri
 // Window table of the shot-aware STGA, one workgroup: every shot
 // [shot_start[s], shot_start[s+1]) is cut into windows of win_t frames (the
 // last one shorter if needed); the shot's first window gets the previous
-// shot's last frame as extra keys, its last window the next shot's first
-// frame.  Boundaries are clamped into [0, T] and at most max_windows entries
-// are written, so malformed boundaries cannot write out of bounds.
+// shot's last `augment` frames as extra keys, its last window the next shot's
+// first `augment` frames (both clipped to those shots).  Boundaries are
+// clamped into [0, T] and at most max_windows entries are written, so
+// malformed boundaries cannot read or write out of bounds.
 constexpr int kShotThreads = 256;
 __global__ __launch_bounds__(kShotThreads) void shot_windows_kernel(const int32_t* __restrict__ shot_start,
                                                                   int n_shots, int T, int win_t, int augment,
@@ -559,11 +635,13 @@ __global__ __launch_bounds__(kShotThreads) void shot_windows_kernel(const int32_
   int base = 0;
   for (int s0 = 0; s0 < n_shots; s0 += kShotThreads) {
     const int s = s0 + tid;
-    int lo = 0, hi = 0, cnt = 0;
+    int lo = 0, hi = 0, cnt = 0, plo = 0, nhi = 0;
     if (s < n_shots) {
       lo = min(max(shot_start[s], 0), T);
       hi = min(max(shot_start[s + 1], lo), T);
       cnt = (hi - lo + win_t - 1) / win_t;
+      plo = s > 0 ? min(max(shot_start[s - 1], 0), lo) : lo;       // previous shot's start
+      nhi = s + 1 < n_shots ? min(max(shot_start[s + 2], hi), T) : hi;  // next shot's end
     }
     scan[tid] = cnt;
     __syncthreads();
@@ -579,8 +657,10 @@ __global__ __launch_bounds__(kShotThreads) void shot_windows_kernel(const int32_
       ShotWindow sw;
       sw.t0 = t0;
       sw.nt = min(win_t, hi - t0);
-      sw.prev = (augment && k == 0 && s > 0 && lo > 0) ? lo - 1 : -1;
-      sw.next = (augment && k == cnt - 1 && s + 1 < n_shots && hi < T) ? hi : -1;
+      sw.pre0 = max(plo, lo - augment);
+      sw.npre = k == 0 ? lo - sw.pre0 : 0;
+      sw.nxt0 = hi;
+      sw.nnxt = k == cnt - 1 ? min(nhi, hi + augment) - hi : 0;
       win[first + k] = sw;
     }
     base += scan[kShotThreads - 1];
@@ -689,7 +769,8 @@ extern "C" int moga_stga_shot_attention(const void* Q, const void* K, const void
   const int64_t N = (int64_t)T * Hs * Ws;
   const int64_t area = (int64_t)tile_h * tile_w;
   if (N >= (int64_t(1) << 31)) return MOGA_ERR_SHAPE;
-  if ((int64_t)(win_t + 2) * area > (int64_t(1) << 20) || !valid_head_dims(H, D)) return MOGA_ERR_UNSUPPORTED;
+  if (augment < 0 || augment > 64) return MOGA_ERR_SHAPE;
+  if ((int64_t)(win_t + 2 * augment) * area > (int64_t(1) << 20) || !valid_head_dims(H, D)) return MOGA_ERR_UNSUPPORTED;
   const size_t need = moga_stga_shot_workspace_bytes(T, n_shots, win_t);
   if (!ws || ws_bytes < need) return MOGA_ERR_WORKSPACE;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
@@ -701,11 +782,33 @@ extern "C" int moga_stga_shot_attention(const void* Q, const void* K, const void
   hipStream_t st = as_stream(stream);
   int* nwin = static_cast<int*>(ws);
   auto* win = reinterpret_cast<ShotWindow*>(static_cast<char*>(ws) + 256);
-  shot_windows_kernel<<<1, kShotThreads, 0, st>>>(shot_start, n_shots, T, win_t, augment != 0, max_windows, win,
-                                                  nwin);
+  shot_windows_kernel<<<1, kShotThreads, 0, st>>>(shot_start, n_shots, T, win_t, augment, max_windows, win, nwin);
   MOGA_LAUNCH_CHECK();
   ShotRows rows{win, nwin, Hs, Ws, tile_h, tile_w, ntx, nspatial, tpg, H};
   const Epilogue epi{alpha, beta, nullptr, nullptr};
   if (D == 128) return launch_attn<128, ShotRows, kEpiScaled>(Q, K, V, O, (int64_t)H * D, scale, epi, rows, items, st);
   return launch_attn<64, ShotRows, kEpiScaled>(Q, K, V, O, (int64_t)H * D, scale, epi, rows, items, st);
+}
+
+extern "C" int moga_group_attention_fused(const void* Q, const void* K, const void* V, const int32_t* cu_seqlens,
+                                          const int32_t* perm, const float* gate, int64_t N, int32_t H, int32_t D,
+                                          int32_t M, float softmax_scale, float beta, void* O, void* ws,
+                                          size_t ws_bytes, void* stream) {
+  using namespace moga;
+  if (!Q || !K || !V || !cu_seqlens || !perm || !gate || !O) return MOGA_ERR_NULL;
+  if (N < 1 || N >= (int64_t(1) << 31) || M < 1 || H < 1 || D < 1) return MOGA_ERR_SHAPE;
+  if (M > kMaxGroups || !valid_head_dims(H, D)) return MOGA_ERR_UNSUPPORTED;
+  const size_t need = moga_workspace_bytes(MOGA_OP_GROUP_ATTENTION, N, M, H, D);
+  if (!ws || ws_bytes < need) return MOGA_ERR_WORKSPACE;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
+  hipStream_t st = as_stream(stream);
+  auto* sched = static_cast<AttnSchedule*>(ws);
+  schedule_kernel<<<1, kWave, 0, st>>>(cu_seqlens, M, H, sched);
+  MOGA_LAUNCH_CHECK();
+  MogaPermRows rows{MogaRows{cu_seqlens, sched, M, H}, perm};
+  const int64_t bound = (ceil_div(N, kBM) + M) * H;
+  const Epilogue epi{1.f, beta, nullptr, gate};
+  if (D == 128)
+    return launch_attn<128, MogaPermRows, kEpiGatedInPlace>(Q, K, V, O, (int64_t)H * D, scale, epi, rows, bound, st);
+  return launch_attn<64, MogaPermRows, kEpiGatedInPlace>(Q, K, V, O, (int64_t)H * D, scale, epi, rows, bound, st);
 }

@@ -33,7 +33,7 @@ def declared_symbols():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
     from sparse_attention_long_router_amd import _lib
@@ -117,6 +117,21 @@ def test_fused_attention_argument_errors(lib):
     assert a(*args[:14], nb - 1, None) == EWS
 
 
+def test_gather_on_load_attention_argument_errors(lib):
+    a = lib.moga_group_attention_fused
+    nb = lib.moga_workspace_bytes(2, 100, 4, 2, 128)
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 100, 2, 128, 4, 0.0, 0.0, FAKE, FAKE, nb, None]
+    assert a(None, *args[1:]) == ENULL                     # Q
+    assert a(*args[:4], None, *args[5:]) == ENULL          # perm
+    assert a(*args[:5], None, *args[6:]) == ENULL          # gate
+    assert a(*args[:12], None, *args[13:]) == ENULL        # O
+    assert a(*args[:6], 0, *args[7:]) == ESHAPE            # N
+    assert a(*args[:9], 65, *args[10:]) == EUNSUP          # M > 64
+    assert a(*args[:8], 48, *args[9:]) == EUNSUP           # D
+    assert a(*args[:13], None, *args[14:]) == EWS
+    assert a(*args[:14], nb - 1, None) == EWS
+
+
 def test_balance_argument_errors(lib):
     b = lib.moga_balance_stats
     nb = lib.moga_workspace_bytes(5, 5000, 8, 1, 64)
@@ -162,5 +177,8 @@ def test_stga_shot_workspace_and_argument_errors(lib):
     assert s(*args(n=0)) == ESHAPE
     assert s(*args(n=7)) == ESHAPE              # more shots than frames
     assert s(*args(D=100)) == EUNSUP
+    aug = args()
+    aug[11] = -1
+    assert s(*aug) == ESHAPE                    # negative augmentation
     assert s(*args(ws=None)) == EWS
     assert s(*args(wsb=need - 1)) == EWS

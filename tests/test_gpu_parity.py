@@ -66,6 +66,10 @@ def _full_check(moga, inp, bias=None, label=""):
     Of = moga.moga_group_attention_unpermute(p["Qp"], p["Kp"], p["Vp"], p["cu_seqlens"], p["perm"], gate)
     torch.cuda.synchronize()
     assert_output_close(_np(Of), ref["O"], "O (fused attention + unpermute)")
+    Og = moga.moga_group_attention_fused(Q, K, V, p["cu_seqlens"], p["perm"], gate)
+    torch.cuda.synchronize()
+    assert_output_close(_np(Og), ref["O"], "O (gather on load)")
+    assert torch.equal(Og, Of)   # same rows, same key order, same arithmetic
     print(f"[parity] {label} Op {e_attn} O {e_out}", flush=True)
     return gid, gate, p, Op, O, ref
 
@@ -116,6 +120,19 @@ def test_fused_unpermute_accumulates(moga):
     assert_output_close(_np(O), ref["O"] + 0.5 * _np(inp["V"]), "fused O + 0.5 V")
 
 
+def test_gather_on_load_accumulates(moga):
+    inp = _inputs("wan13b_21f", N=2600, H=2, D=128, M=5, d_model=256)
+    gid, gate = moga.moga_route(inp["X"], inp["Wr"])
+    p = moga.moga_permute(gid, 5)                       # sort only, no gathered copies
+    assert p["Qp"] is None
+    prev = inp["V"].clone()
+    O = moga.moga_group_attention_fused(inp["Q"], inp["K"], inp["V"], p["cu_seqlens"], p["perm"], gate,
+                                        beta=0.5, O=prev)
+    torch.cuda.synchronize()
+    ref = oracle.moga_forward(*(_np(inp[k]) for k in ("X", "Wr", "Q", "K", "V")), 5)
+    assert_output_close(_np(O), ref["O"] + 0.5 * _np(inp["V"]), "gather-on-load O + 0.5 V")
+
+
 def test_unpermute_accumulate(moga):
     inp = _inputs("wan13b_21f", N=2500, H=2, D=64, M=5, d_model=128)
     gid, gate = moga.moga_route(inp["X"], inp["Wr"])
@@ -150,11 +167,13 @@ def test_stga(moga, T, Hs, Ws, win_t, th, tw, H, D, alpha, beta):
 
 
 @pytest.mark.parametrize("T,Hs,Ws,shots,win_t,th,tw,aug,H,D,alpha,beta", [
-    (7, 6, 10, [0, 3, 4, 7], 2, 3, 5, True, 2, 128, 1.0, 0.0),    # a one-frame shot, ragged windows
-    (9, 30, 52, [0, 5, 9], 3, 30, 26, True, 1, 128, 0.5, 0.5),    # Wan-like frames, 780-token tiles
-    (8, 8, 8, [0, 2, 3, 8], 3, 4, 8, False, 2, 64, 1.0, 1.0),     # no augmentation
-    (6, 4, 4, [0, 6], 2, 4, 4, True, 1, 64, 1.0, 0.0),            # one shot: plain windows
-    (5, 4, 8, [0, 1, 2, 3, 4, 5], 4, 2, 4, True, 2, 128, 1.0, 0.0),  # every frame its own shot
+    (7, 6, 10, [0, 3, 4, 7], 2, 3, 5, 1, 2, 128, 1.0, 0.0),     # a one-frame shot, ragged windows
+    (9, 30, 52, [0, 5, 9], 3, 30, 26, 1, 1, 128, 0.5, 0.5),     # Wan-like frames, 780-token tiles
+    (8, 8, 8, [0, 2, 3, 8], 3, 4, 8, 0, 2, 64, 1.0, 1.0),       # no augmentation
+    (6, 4, 4, [0, 6], 2, 4, 4, 1, 1, 64, 1.0, 0.0),             # one shot: plain windows
+    (5, 4, 8, [0, 1, 2, 3, 4, 5], 4, 2, 4, 1, 2, 128, 1.0, 0.0),  # every frame its own shot
+    (12, 6, 10, [0, 1, 5, 6, 12], 3, 6, 5, 2, 2, 128, 1.0, 0.0),  # two frames per side, clipped
+    (10, 30, 52, [0, 4, 10], 3, 30, 26, 3, 1, 128, 1.0, 0.0),   # three per side, Wan-like tile
 ])
 def test_stga_shot(moga, T, Hs, Ws, shots, win_t, th, tw, aug, H, D, alpha, beta):
     N = T * Hs * Ws
@@ -176,13 +195,16 @@ def test_stga_shot(moga, T, Hs, Ws, shots, win_t, th, tw, aug, H, D, alpha, beta
 # Full workload sizes, in the launch configuration the benchmark times
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["wan13b_21f", "clip30s_122f", "wan14b_122f", "minute_372f"])
-def test_full_size_sampled(moga, name):
+@pytest.mark.parametrize("name,path", [("wan13b_21f", "fused_epilogue"), ("clip30s_122f", "fused_epilogue"),
+                                       ("clip30s_122f", "gather_on_load"), ("clip30s_122f", "separate"),
+                                       ("wan14b_122f", "fused_epilogue"), ("minute_372f", "fused_epilogue"),
+                                       ("minute_372f", "gather_on_load")])
+def test_full_size_sampled(moga, name, path):
     wl = get_workload(name)
-    print(f"[parity] full {name} N={wl.N} d={wl.d_model} H={wl.H} M={wl.M}", flush=True)
+    print(f"[parity] full {name} path={path} N={wl.N} d={wl.d_model} H={wl.H} M={wl.M}", flush=True)
     inp = make_inputs(wl, device=DEV)
     X, Wr, Q, K, V = (inp[k] for k in ("X", "Wr", "Q", "K", "V"))
-    fwd = moga.MogaForward(wl.N, wl.d_model, wl.H, wl.D, wl.M, DEV, stga=wl.stga)
+    fwd = moga.MogaForward(wl.N, wl.d_model, wl.H, wl.D, wl.M, DEV, stga=wl.stga, path=path)
     O = fwd(X, Wr, Q, K, V)
     torch.cuda.synchronize()
 

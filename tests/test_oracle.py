@@ -322,12 +322,15 @@ def test_moga_plus_stga_is_sum_of_branches():
 def test_shot_windows_hand_example():
     # 10 frames, shots [0,4) [4,5) [5,10), windows of 3 frames
     w = oracle.shot_windows([0, 4, 5, 10], 3)
-    assert w == [(0, 3, -1, -1), (3, 1, -1, 4), (4, 1, 3, 5), (5, 3, 4, -1), (8, 2, -1, -1)]
-    assert oracle.shot_windows([0, 4, 5, 10], 3, aug=False) == [(0, 3, -1, -1), (3, 1, -1, -1), (4, 1, -1, -1),
-                                                                (5, 3, -1, -1), (8, 2, -1, -1)]
+    assert w == [(0, 3, [], []), (3, 1, [], [4]), (4, 1, [3], [5]), (5, 3, [4], []), (8, 2, [], [])]
+    assert oracle.shot_windows([0, 4, 5, 10], 3, aug=False) == [(0, 3, [], []), (3, 1, [], []), (4, 1, [], []),
+                                                                (5, 3, [], []), (8, 2, [], [])]
+    # two frames per side, clipped to the one-frame middle shot
+    assert oracle.shot_windows([0, 4, 5, 10], 3, aug=2) == [(0, 3, [], []), (3, 1, [], [4]), (4, 1, [2, 3], [5, 6]),
+                                                            (5, 3, [4], []), (8, 2, [], [])]
 
 
-def _shot_mask(T, Hs, Ws, shot_start, win_t, th, tw):
+def _shot_mask(T, Hs, Ws, shot_start, win_t, th, tw, aug=1):
     """Allowed (query, key) pairs restated token by token from the STGA rules."""
     N = T * Hs * Ws
     shot = np.zeros(T, int)
@@ -346,8 +349,8 @@ def _shot_mask(T, Hs, Ws, shot_start, win_t, th, tw):
                 continue
             same = shot[u] == shot[t] and win(u)[0] == win(t)[0]
             k, first, last = win(t)
-            prev = first and shot[t] > 0 and u == shot_start[shot[t]] - 1
-            nxt = last and shot[t] < len(shot_start) - 2 and u == shot_start[shot[t] + 1]
+            prev = first and shot[u] == shot[t] - 1 and shot_start[shot[t]] - u <= aug
+            nxt = last and shot[u] == shot[t] + 1 and u - shot_start[shot[t] + 1] < aug
             mask[n, m] = same or prev or nxt
     return mask
 
@@ -358,9 +361,10 @@ def check_stga_shot_masked():
     shots = [0, 3, 4, 7]
     N = T * Hs * Ws
     Q, K, V = (r.standard_normal((N, H, D)) for _ in range(3))
-    out = oracle.stga_shot_attention(Q, K, V, T, Hs, Ws, shots, 2, 1, 2, 0.3)
-    ref = _sdpa(Q, K, V, _shot_mask(T, Hs, Ws, shots, 2, 1, 2), scale=0.3)
-    np.testing.assert_allclose(out, ref, atol=1e-12)
+    for aug in (1, 2):
+        out = oracle.stga_shot_attention(Q, K, V, T, Hs, Ws, shots, 2, 1, 2, 0.3, aug)
+        ref = _sdpa(Q, K, V, _shot_mask(T, Hs, Ws, shots, 2, 1, 2, aug), scale=0.3)
+        np.testing.assert_allclose(out, ref, atol=1e-12)
     # one shot and windows that tile it: the plain STGA windows
     plain = oracle.stga_shot_attention(Q, K, V, T, Hs, Ws, [0, T], 7, 2, 2, 0.3)
     np.testing.assert_allclose(plain, _sdpa(Q, K, V, oracle.stga_group_ids(T, Hs, Ws, 7, 2, 2)[:, None]
@@ -378,9 +382,9 @@ def test_stga_shot_rows_match_masked_attention():
     shots = [0, 1, 4, 6]
     N = T * Hs * Ws
     Q, K, V = (r.standard_normal((N, H, D)) for _ in range(3))
-    for aug in (True, False):
+    for aug in (1, 2, 0):
         rows = oracle.stga_shot_attention_rows(Q, K, V, T, Hs, Ws, shots, 2, 2, 1, 0.7, np.arange(N), aug)
-        mask = _shot_mask(T, Hs, Ws, shots, 2, 2, 1)
+        mask = _shot_mask(T, Hs, Ws, shots, 2, 2, 1, aug)
         if not aug:
             wid = np.array([w for w, (t0, nt, _, _) in enumerate(oracle.shot_windows(shots, 2, False))
                             for _ in range(nt)])
@@ -463,13 +467,13 @@ def _off_by_one_cu(group_id, M):
     return perm, cu, mx
 
 
-def _windows_ignore_shots(shot_start, win_t, aug=True):
+def _windows_ignore_shots(shot_start, win_t, aug=1):
     return _orig_shot_windows([shot_start[0], shot_start[-1]], win_t, aug)
 
 
-def _augment_wrong_frames(shot_start, win_t, aug=True):
+def _augment_wrong_frames(shot_start, win_t, aug=1):
     # the adjacent frames taken one step too far into the neighbouring shots
-    return [(t0, nt, p - 1 if p > 0 else p, n + 1 if 0 <= n < shot_start[-1] - 1 else n)
+    return [(t0, nt, [f - 1 for f in p], [f + 1 for f in n])
             for t0, nt, p, n in _orig_shot_windows(shot_start, win_t, aug)]
 
 
