@@ -204,14 +204,17 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // Softmax bookkeeping of one 32-query block (one query per lane; the two wave
 // halves hold the same query).  The exponent offset m_ref is fixed from the
-// row's first 32 keys and never moves, so the output accumulator is never
-// rescaled; a later score more than 2^kTau above it raises `over`, and the
-// work item is then recomputed with the exact row max (see attn_kernel).
+// row's first 32 keys before the key loop and never moves, so the output
+// accumulator is never rescaled and no per-tile row max is needed.  Weights
+// above 1 (later scores above the first keys' max) keep their relative
+// precision in float32 and bf16; only a denominator that reaches 2^kLogLimit
+// (or overflows) could lose the output, and the work item is then recomputed
+// with the exact row max (see attn_kernel).
 struct RowState {
-  float m_ref;  // exponent offset (log2 domain); -inf until the first keys
+  float m_ref;  // exponent offset (log2 domain)
   float l;      // this lane's share of the denominator
 };
-constexpr float kTau = 32.0f;
+constexpr float kLimit = 18446744073709551616.0f;  // 2^64
 
 // max / sum of a value over the two wave halves (lanes c and c+32 share a query)
 __device__ __forceinline__ float halves_max(float v) {
@@ -289,14 +292,7 @@ __device__ __forceinline__ void issue_tile_idx(const uint16_t* __restrict__ K, c
 // Softmax step of one query block over one 32-key half of a tile: bf16 P^T
 // operands of the half's two 16-key MFMA steps go to pb, their sum to st.l.
 // s: reg r is key 8*(r/4) + 4*hh + r%4 of the half (masked keys are -inf).
-__device__ __forceinline__ void softmax_half(const f32x16& s, RowState& st, float scale_log2, bf16x8 (&pb)[2],
-                                             bool& over) {
-  float mx = s[0];
-#pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-  const float m_new = halves_max(mx) * scale_log2;
-  st.m_ref = st.m_ref == -INFINITY ? m_new : st.m_ref;
-  over |= m_new > st.m_ref + kTau;
+__device__ __forceinline__ void softmax_half(const f32x16& s, RowState& st, float scale_log2, bf16x8 (&pb)[2]) {
   float rs = 0.f;
 #pragma unroll
   for (int t = 0; t < 2; ++t)
@@ -378,7 +374,7 @@ __device__ __forceinline__ void mask_half(f32x16 (&s)[QB], int key0, int len, in
 template <int D, int QB, bool kMask>
 __device__ __forceinline__ void tile_step(const uint16_t* Ks, const uint16_t* Vs, int k0, int len,
                                           const bf16x8 (&qf)[QB][D / 16], f32x16 (&o)[QB][D / 32],
-                                          RowState (&rs)[QB], float scale_log2, int lane, bool& over) {
+                                          RowState (&rs)[QB], float scale_log2, int lane) {
   const int hh = lane >> 5;
   f32x16 s0[QB], s1[QB];
   bf16x8 p[QB][2];
@@ -386,11 +382,11 @@ __device__ __forceinline__ void tile_step(const uint16_t* Ks, const uint16_t* Vs
   qk_half<D, QB>(Ks, qf, 1, lane, s1);
   mask_half<kMask, QB>(s0, k0, len, hh);
 #pragma unroll
-  for (int b = 0; b < QB; ++b) softmax_half(s0[b], rs[b], scale_log2, p[b], over);
+  for (int b = 0; b < QB; ++b) softmax_half(s0[b], rs[b], scale_log2, p[b]);
   pv_half<D, QB>(Vs, p, 0, lane, o);
   mask_half<kMask, QB>(s1, k0 + 32, len, hh);
 #pragma unroll
-  for (int b = 0; b < QB; ++b) softmax_half(s1[b], rs[b], scale_log2, p[b], over);
+  for (int b = 0; b < QB; ++b) softmax_half(s1[b], rs[b], scale_log2, p[b]);
   pv_half<D, QB>(Vs, p, 1, lane, o);
 }
 
@@ -479,9 +475,8 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave) void attn_kernel(
   for (int b = 0; b < QB; ++b) {
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) o[b][db] = f32x16{};
-    rs[b] = {-INFINITY, 0.f};
+    rs[b] = {0.f, 0.f};
   }
-  bool over = false;
 
   // Tile t lives in buffer t % 2.  At the top of each tile: wait for this
   // wave's loads, barrier (all waves' loads landed, tile t-1 fully consumed),
@@ -502,7 +497,7 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave) void attn_kernel(
       if constexpr (kMax)
         tile_max<D, QB, kMask>(Ks, t * kBN, w.len, qf, mx, lane);
       else
-        tile_step<D, QB, kMask>(Ks, Vs, t * kBN, w.len, qf, o, rs, scale_log2, lane, over);
+        tile_step<D, QB, kMask>(Ks, Vs, t * kBN, w.len, qf, o, rs, scale_log2, lane);
     };
     using F = std::false_type;
     using T = std::true_type;
@@ -529,11 +524,29 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave) void attn_kernel(
       for (int b = 0; b < QB; ++b) rs[b] = {halves_max(mx[b]) * scale_log2, 0.f};
     }
   };
+  // Exponent offsets from each row's first 32 keys (key 0 always exists).
+  {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    f32x16 s[QB];
+    qk_half<D, QB>(Ks0, qf, 0, lane, s);
+    if (w.len < 32) mask_half<true, QB>(s, 0, w.len, hh);
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      float mx = s[b][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
+      rs[b].m_ref = halves_max(mx) * scale_log2;
+    }
+  }
   run(std::false_type{});
 
-  // A score far above a row's first keys would overflow the fixed offset:
-  // recompute this work item exactly (row maxima first, then softmax and P V
-  // with the exact maxima, where no score exceeds its offset).
+  // Scores far above a row's first keys would overflow the fixed offset (the
+  // denominator is not finite or reaches kLimit): recompute this work item
+  // exactly (row maxima first, then softmax and P V with the exact maxima).
+  bool over = false;
+#pragma unroll
+  for (int b = 0; b < QB; ++b) over |= !(halves_sum(rs[b].l) < kLimit);
   if (__syncthreads_or(over)) {
     __syncthreads();
     if constexpr (Rows::kIndirect) fetch_keys<D, NW>(rows, w, 0, wave, lane, kidx);

@@ -261,12 +261,15 @@ def test_full_size_visual_block(moga):
     print(f"[parity] visual block: {rows.size} rows, {e}", flush=True)
 
 
-@pytest.mark.parametrize("late,label", [(2.0, "overflow-fallback"), (0.9, "fixed-offset")])
+@pytest.mark.parametrize("late,label", [(4.0, "float32-overflow"), (2.0, "overflow-fallback"),
+                                        (0.9, "fixed-offset")])
 def test_attention_score_growth(moga, late, label):
-    """Scores that grow far beyond a row's first keys: with late = 2, q.k jumps
-    from 0 to ~512 (about 65 in log2 units after scaling) and the exact
-    recomputation path must engage; with late = 0.9 the growth stays inside
-    the fixed-offset range (2^32) and the main path handles it."""
+    """Scores that grow far beyond a row's first keys (which fix the exponent
+    offset): with late = 2, q.k jumps from 0 to ~512, about 65 in log2 units
+    after scaling, so the denominator passes 2^64 and the exact recomputation
+    must engage; with late = 4 (~130 log2 units) the weights themselves would
+    overflow float32 without it; with late = 0.9 (~29 log2 units) the main
+    path keeps the large weights and must still be exact."""
     print(f"[parity] score growth {label}", flush=True)
     N, H, D = 700, 2, 128
     g = torch.Generator().manual_seed(7)
