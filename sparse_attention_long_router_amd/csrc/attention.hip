@@ -38,6 +38,13 @@
 
 #include "moga_internal.h"
 
+// LLVM's raw buffer load to LDS (buffer_load_dwordx4 ... lds): descriptor,
+// LDS base (M0), bytes per lane, per-lane byte offset, scalar offset,
+// immediate offset, cache policy.
+typedef int32_t i32x4v __attribute__((ext_vector_type(4)));
+__device__ void raw_buffer_load_lds(i32x4v rsrc, __attribute__((address_space(3))) void* lds, int size, int voffset,
+                                    int soffset, int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
 namespace moga {
 namespace {
 
@@ -63,6 +70,7 @@ struct Work {
 // Learned groups: rows of group g are cu[g] .. cu[g+1]-1 of the permuted tensors.
 struct MogaRows {
   static constexpr bool kIndirect = false;
+  static constexpr bool kContiguous = true;  // key row i of a group is row0 + i
   const int32_t* cu;
   const AttnSchedule* sched;
   int M, H;
@@ -92,6 +100,7 @@ struct MogaRows {
 // gathered copies exist.  Key rows are fetched a tile ahead (kIndirect).
 struct MogaPermRows {
   static constexpr bool kIndirect = true;
+  static constexpr bool kContiguous = false;
   MogaRows base;
   const int32_t* perm;
   __device__ __forceinline__ bool decode(int item, Work& w) const { return base.decode(item, w); }
@@ -102,6 +111,7 @@ struct MogaPermRows {
 // Static windows over frame-major tokens n = (t*Hs + y)*Ws + x.
 struct StgaRows {
   static constexpr bool kIndirect = false;
+  static constexpr bool kContiguous = false;
   int Hs, Ws, win_t, tile_h, tile_w, nty, ntx, tiles_per_group, H, items;
   __device__ __forceinline__ bool decode(int item, Work& w) const {
     if (item >= items) return false;
@@ -146,6 +156,7 @@ struct ShotWindow {
 // tiles sharing one key set are consecutive (and land on one XCD).
 struct ShotRows {
   static constexpr bool kIndirect = false;
+  static constexpr bool kContiguous = false;
   const ShotWindow* win;
   const int* nwin;
   int Hs, Ws, tile_h, tile_w, ntx, nspatial, tpg, H;
@@ -249,6 +260,43 @@ __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ K, const
                                      16, 0, 0);
     __builtin_amdgcn_global_load_lds((global_void*)(V + base + (p ^ vswz(r, CPR)) * 8), (lds_void*)(Vs + lds_off),
                                      16, 0, 0);
+  }
+}
+
+// Contiguous-row variant of issue_tile: buffer loads straight to LDS.  The
+// tile's first row and the group's remaining bytes live in a scalar buffer
+// descriptor, so a lane's byte offset (row in tile, swizzled chunk) is the
+// same for every tile and no per-tile address arithmetic runs on the VALU;
+// rows past the group end fail the descriptor's range check and land in LDS
+// as zeros (their scores are masked).
+// Descriptor of rows [first, first + n) of one head: base address, stride 0,
+// byte range, and the gfx9 raw-buffer data format word.
+__device__ __forceinline__ i32x4v row_range_rsrc(const uint16_t* base, int64_t n_rows, int64_t row_bytes,
+                                                 int bytes_per_row) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  int64_t range = n_rows > 0 ? (n_rows - 1) * row_bytes + bytes_per_row : 0;
+  range = range < 0xffffffffll ? range : 0xffffffffll;
+  i32x4v r;
+  r[0] = (int32_t)(uint32_t)a;
+  r[1] = (int32_t)(uint32_t)(a >> 32);
+  r[2] = (int32_t)(uint32_t)range;
+  r[3] = 0x00020000;
+  return r;
+}
+
+template <int D, int NW>
+__device__ __forceinline__ void issue_tile_buf(i32x4v krs, i32x4v vrs, uint16_t* Ks, uint16_t* Vs,
+                                               int64_t row_stride, int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int LOADS = kBN * CPR / (NW * kWave);
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) {
+    const int q = (wave * LOADS + j) * kWave + lane;
+    const int r = q / CPR, p = q % CPR;
+    const int rb = r * (int)row_stride * 2;
+    const int lds_off = (wave * LOADS + j) * kWave * 8;
+    raw_buffer_load_lds(krs, (lds_void*)(Ks + lds_off), 16, rb + ((p ^ kswz(r, CPR)) << 4), 0, 0, 0);
+    raw_buffer_load_lds(vrs, (lds_void*)(Vs + lds_off), 16, rb + ((p ^ vswz(r, CPR)) << 4), 0, 0, 0);
   }
 }
 
@@ -445,7 +493,12 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave) void attn_kernel(
   // Tile t's K/V loads; with gather on load, also fetch tile t+1's key rows.
   [[maybe_unused]] int32_t kidx[tile_loads<D, NW>()];
   auto issue = [&](uint16_t* Kd, uint16_t* Vd, int t) {
-    if constexpr (Rows::kIndirect) {
+    if constexpr (Rows::kContiguous) {
+      const int64_t first = (w.row0 + (int64_t)t * kBN) * row_stride + hoff;
+      const int64_t n_rows = w.len - t * kBN;
+      issue_tile_buf<D, NW>(row_range_rsrc(K + first, n_rows, row_stride * 2, D * 2),
+                            row_range_rsrc(V + first, n_rows, row_stride * 2, D * 2), Kd, Vd, row_stride, wave, lane);
+    } else if constexpr (Rows::kIndirect) {
       issue_tile_idx<D, NW>(K, V, Kd, Vd, kidx, row_stride, hoff, wave, lane);
       if (t + 1 < ntiles) fetch_keys<D, NW>(rows, w, (t + 1) * kBN, wave, lane, kidx);
     } else {
