@@ -25,6 +25,7 @@ from .moga_oracle import (  # noqa: F401
     moga_forward,
     moga_output_rows,
     balance_stats,
+    moga_backward,
     shot_windows,
     stga_shot_attention,
     stga_shot_attention_rows,

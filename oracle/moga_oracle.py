@@ -56,6 +56,7 @@ __all__ = [
     "moga_forward",
     "moga_output_rows",
     "balance_stats",
+    "moga_backward",
     "shot_windows",
     "stga_shot_attention",
     "stga_shot_attention_rows",
@@ -437,3 +438,71 @@ def balance_stats(group_id, gate, M: int, alpha: float = 0.1):
     F = np.bincount(g, minlength=M).astype(np.float64) / N
     P = np.bincount(g, weights=_f64(gate), minlength=M) / N
     return F, P, alpha * M * float(np.sum(F * P))
+
+
+# ---------------------------------------------------------------------------
+# Backward pass ("Grouped Attention" section: the gate p(g|x) is the gradient
+# path to the router; Eq. 1 and Eq. 3 differentiated by the chain rule)
+# ---------------------------------------------------------------------------
+
+def moga_backward(X, Wr, Q, K, V, M: int, dO, scale=None, bias=None):
+    """Gradients of L = sum(O * dO) for the MoGA output O[n] = p_n * SA_n,
+    with p_n = softmax(r_n)[g_n], r_n = X_n W_r^T (+ b) and the hard choice
+    g_n = argmax r_n held fixed (it has no gradient).  Everything in float64.
+
+    Written out from the chain rule:
+      dgate_n   = <dO_n, SA_n>                    (over heads and channels)
+      dSA_n     = p_n * dO_n
+      per group and head, with P = softmax(scale Q K^T) and A = P V:
+        dV = P^T dA,  dP = dA V^T,  dS = P * (dP - rowsum(dA * A)),
+        dQ = scale dS K,  dK = scale dS^T Q
+      dr_nj     = dgate_n * p_n * ([j == g_n] - softmax(r_n)_j)
+      dX = dr W_r,  dW_r = dr^T X,  db = sum_n dr_n.
+    Returns a dict with dQ, dK, dV [N, H, D], dX [N, d_model], dWr [M, d_model],
+    dbias [M], dgate [N], plus the forward pieces the GPU backward consumes
+    (permuted SA output Op, per-row log-sum-exp lse [H, N] of the scaled scores,
+    and delta [H, N] = rowsum(dSA * SA) in permuted order).
+    """
+    X, Wr, Q, K, V, dO = (_f64(a) for a in (X, Wr, Q, K, V, dO))
+    N, H, D = Q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    r = router_logits(X, Wr, bias)
+    g = np.argmax(r.astype(np.float32), axis=1)
+    e = np.exp(r - r.max(axis=1, keepdims=True))
+    prob = e / e.sum(axis=1, keepdims=True)
+    p = prob[np.arange(N), g]
+    perm, cu, _ = permute(g, M)
+    dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+    Op = np.zeros((N, H, D))
+    lse = np.zeros((H, N))
+    delta = np.zeros((H, N))
+    dgate = np.zeros(N)
+    for i in range(M):
+        rows = perm[cu[i]:cu[i + 1]]
+        if rows.size == 0:
+            continue
+        for h in range(H):
+            q, k, v = Q[rows, h], K[rows, h], V[rows, h]
+            S = scale * (q @ k.T)
+            mx = S.max(axis=1, keepdims=True)
+            P = np.exp(S - mx)
+            den = P.sum(axis=1, keepdims=True)
+            P /= den
+            A = P @ v
+            dA = p[rows, None] * dO[rows, h]
+            dgate[rows] += np.sum(dO[rows, h] * A, axis=1)
+            dV[rows, h] = P.T @ dA
+            dP = dA @ v.T
+            dl = np.sum(dA * A, axis=1, keepdims=True)
+            dS = P * (dP - dl)
+            dQ[rows, h] = scale * (dS @ k)
+            dK[rows, h] = scale * (dS.T @ q)
+            Op[cu[i]:cu[i + 1], h] = A
+            lse[h, cu[i]:cu[i + 1]] = (mx + np.log(den))[:, 0]
+            delta[h, cu[i]:cu[i + 1]] = dl[:, 0]
+    onehot = np.zeros_like(prob)
+    onehot[np.arange(N), g] = 1.0
+    dr = (dgate * p)[:, None] * (onehot - prob)
+    return {"dQ": dQ, "dK": dK, "dV": dV, "dX": dr @ _f64(Wr), "dWr": dr.T @ X, "dbias": dr.sum(axis=0),
+            "dgate": dgate, "dlogits": dr, "group_id": g.astype(np.int32), "gate": p, "perm": perm,
+            "cu_seqlens": cu, "Op": Op, "lse": lse, "delta": delta}

@@ -411,6 +411,74 @@ def test_frame_attention_and_visual_mean():
 
 
 # ---------------------------------------------------------------------------
+# Backward pass: pinned against float64 autograd of an independent dense
+# formulation (same-group mask, router softmax, gate times attention)
+# ---------------------------------------------------------------------------
+
+def _autograd_grads(X, Wr, Q, K, V, dO, bias, g, scale):
+    t = lambda a: torch.tensor(np.asarray(a, dtype=np.float64), requires_grad=True)  # noqa: E731
+    Xt, Wt, Qt, Kt, Vt = t(X), t(Wr), t(Q), t(K), t(V)
+    bt = t(np.zeros(Wr.shape[0]) if bias is None else bias)
+    gt = torch.tensor(np.asarray(g, dtype=np.int64))
+    prob = torch.softmax(Xt @ Wt.T + bt, dim=1)
+    p = prob[torch.arange(X.shape[0]), gt]
+    mask = gt[:, None] == gt[None, :]
+    outs = []
+    for h in range(Q.shape[1]):
+        S = scale * (Qt[:, h] @ Kt[:, h].T)
+        S = S.masked_fill(~mask, float("-inf"))
+        outs.append(torch.softmax(S, dim=1) @ Vt[:, h])
+    O = p[:, None, None] * torch.stack(outs, dim=1)
+    (O * torch.tensor(dO)).sum().backward()
+    return {"dQ": Qt.grad.numpy(), "dK": Kt.grad.numpy(), "dV": Vt.grad.numpy(), "dX": Xt.grad.numpy(),
+            "dWr": Wt.grad.numpy(), "dbias": bt.grad.numpy()}
+
+
+def check_backward_autograd(seed=30, bias=True):
+    X, Wr, Q, K, V, b = _random_case(seed, N=90, d=20, M=4, H=2, D=8, bias=bias)
+    dO = _rng(seed + 100).standard_normal(Q.shape)
+    out = oracle.moga_backward(X, Wr, Q, K, V, 4, dO, scale=0.4, bias=b)
+    ref = _autograd_grads(X, Wr, Q, K, V, dO, b, out["group_id"], 0.4)
+    for k, v in ref.items():
+        np.testing.assert_allclose(out[k], v, rtol=1e-9, atol=1e-11, err_msg=k)
+
+
+def test_backward_matches_autograd():
+    check_backward_autograd()
+    check_backward_autograd(seed=31, bias=False)
+
+
+def test_backward_single_group_router_gradient_vanishes():
+    # M = 1: p == 1 for every token and its derivative is zero
+    X, Wr, Q, K, V, _ = _random_case(32, N=40, M=1)
+    dO = _rng(33).standard_normal(Q.shape)
+    out = oracle.moga_backward(X, Wr, Q, K, V, 1, dO)
+    assert np.abs(out["dX"]).max() == 0 and np.abs(out["dWr"]).max() == 0 and np.abs(out["dbias"]).max() == 0
+
+
+def test_backward_constant_values_give_no_query_key_gradient():
+    # V rows equal inside a group: attention returns that row for any weights
+    X, Wr, Q, K, _, _ = _random_case(34, N=50, M=3)
+    V = np.broadcast_to(_rng(35).standard_normal((1, Q.shape[1], Q.shape[2])), Q.shape).copy()
+    out = oracle.moga_backward(X, Wr, Q, K, V, 3, _rng(36).standard_normal(Q.shape))
+    assert np.abs(out["dQ"]).max() < 1e-12 and np.abs(out["dK"]).max() < 1e-12
+
+
+def test_backward_lse_and_delta_definitions():
+    X, Wr, Q, K, V, _ = _random_case(37, N=30, M=2, H=1, D=4)
+    dO = _rng(38).standard_normal(Q.shape)
+    out = oracle.moga_backward(X, Wr, Q, K, V, 2, dO)
+    perm, cu = out["perm"], out["cu_seqlens"]
+    scale = 0.5
+    j = int(cu[1])                     # first row of group 1
+    grp = perm[cu[1]:cu[2]]
+    n = perm[j]
+    s = [math.fsum(Q[n, 0, c] * K[m, 0, c] for c in range(4)) * scale for m in grp]
+    assert abs(out["lse"][0, j] - math.log(math.fsum(math.exp(x) for x in s))) < 1e-12
+    assert abs(out["delta"][0, j] - out["gate"][n] * float(np.dot(dO[n, 0], out["Op"][j, 0]))) < 1e-12
+
+
+# ---------------------------------------------------------------------------
 # Group-balancing statistics (Eq. 6)
 # ---------------------------------------------------------------------------
 
@@ -477,9 +545,35 @@ def _augment_wrong_frames(shot_start, win_t, aug=1):
             for t0, nt, p, n in _orig_shot_windows(shot_start, win_t, aug)]
 
 
+def _backward_no_delta(*a, **k):
+    out = _orig_backward(*a, **k)   # dS = P * dP (delta term dropped) changes dQ and dK
+    X, Wr, Q, K, V, M, dO = a[:7]
+    scale = k.get("scale") or 1.0 / math.sqrt(Q.shape[2])
+    perm, cu = out["perm"], out["cu_seqlens"]
+    for i in range(M):
+        rows = perm[cu[i]:cu[i + 1]]
+        for h in range(Q.shape[1]):
+            P = np.exp(scale * Q[rows, h] @ K[rows, h].T - out["lse"][h, cu[i]:cu[i + 1], None])
+            out["dQ"][rows, h] += scale * (P * out["delta"][h, cu[i]:cu[i + 1], None]) @ K[rows, h]
+    return out
+
+
+def _backward_router_sign(*a, **k):
+    out = _orig_backward(*a, **k)
+    out["dX"], out["dWr"], out["dbias"] = -out["dX"], -out["dWr"], -out["dbias"]
+    return out
+
+
+def _backward_unscaled_dk(*a, **k):
+    out = _orig_backward(*a, **k)
+    out["dK"] = out["dK"] / (k.get("scale") or 1.0 / math.sqrt(a[2].shape[2]))
+    return out
+
+
 _orig_permute = om.permute
 _orig_unpermute = om.unpermute
 _orig_shot_windows = om.shot_windows
+_orig_backward = om.moga_backward
 
 MUTANTS = [
     ("_softmax_rows_times_v", _wrong_scale, [check_moga_is_gated_masked_attention, check_bruteforce_loops]),
@@ -490,6 +584,9 @@ MUTANTS = [
     ("unpermute", _ungated_unpermute, [check_moga_is_gated_masked_attention, check_bruteforce_loops]),
     ("shot_windows", _windows_ignore_shots, [check_stga_shot_masked]),
     ("shot_windows", _augment_wrong_frames, [check_stga_shot_masked]),
+    ("moga_backward", _backward_no_delta, [check_backward_autograd]),
+    ("moga_backward", _backward_router_sign, [check_backward_autograd]),
+    ("moga_backward", _backward_unscaled_dk, [check_backward_autograd]),
 ]
 
 
