@@ -55,7 +55,9 @@ typedef enum moga_op {
   MOGA_OP_GROUP_ATTENTION = 2,
   MOGA_OP_UNPERMUTE = 3,
   MOGA_OP_STGA_ATTENTION = 4,
-  MOGA_OP_BALANCE_STATS = 5
+  MOGA_OP_BALANCE_STATS = 5,
+  MOGA_OP_ROUTE_BACKWARD = 6,     /* pass d_model as D */
+  MOGA_OP_ATTENTION_BACKWARD = 7
 } moga_op;
 
 /*
@@ -211,6 +213,70 @@ size_t moga_stga_shot_workspace_bytes(int32_t T, int32_t n_shots, int32_t win_t)
  */
 int moga_balance_stats(const int32_t* group_id, const float* gate, int64_t N, int32_t M, float alpha,
                        float* F, float* P, float* loss, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * ---- Backward pass ----
+ * Gradients of L = sum(O * dO) for the MoGA output O[n] = gate[n] * SA(n)
+ * ("Grouped Attention" section: the gate p(g(x)|x) is the router's gradient
+ * path, the hard argmax has none).  A training step runs
+ *   moga_route -> moga_permute -> moga_group_attention_train (saves Op, lse)
+ *   -> moga_unpermute (O) ... and back:
+ *   moga_unpermute_backward -> moga_group_attention_backward -> moga_route_backward.
+ */
+
+/*
+ * moga_group_attention_train -- moga_group_attention that also saves, for the
+ *   backward pass, lse[h][j] = log sum_k exp(scale * q_jh . k_kh) over row j's
+ *   group (natural log), float [H, N] (head-major, permuted rows).  Other
+ *   arguments and ws as moga_group_attention.
+ */
+int moga_group_attention_train(const void* Qp, const void* Kp, const void* Vp,
+                               const int32_t* cu_seqlens, int64_t N, int32_t H, int32_t D,
+                               int32_t M, float softmax_scale, void* Op, float* lse,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moga_unpermute_backward -- backward of O[perm[j]] = gate[perm[j]] * Op[j]:
+ *   dgate[n]    = sum over heads and channels of dO[n] * Op[j]  (n = perm[j]), float [N]
+ *   dOp[j]      = gate[n] * dO[n]                               bf16 [N, H, D] (permuted)
+ *   delta[h][j] = sum over channels of dOp[j, h] * Op[j, h]    float [H, N]
+ *   (delta computed from the bf16-rounded dOp the attention backward reads,
+ *   so that its dP - delta cancels exactly where it should).  dO bf16 [N, H, D] in
+ *   original order; Op the saved attention output.  Needs no workspace.
+ */
+int moga_unpermute_backward(const void* dO, const void* Op, const int32_t* perm, const float* gate,
+                            int64_t N, int32_t H, int32_t D, void* dOp, float* delta, float* dgate,
+                            void* stream);
+
+/*
+ * moga_group_attention_backward -- gradients of the group attention (Eq. 1
+ *   inside each group): with P = exp(scale Q K^T - lse) per group and head,
+ *   dV = P^T dOp, dS = P * (dOp V^T - delta), dQ = scale dS K,
+ *   dK = scale dS^T Q.  Inputs in permuted order (Qp, Kp, Vp, dOp bf16
+ *   [N, H, D]; lse, delta float [H, N]); outputs dQ, dK, dV bf16 [N, H, D]
+ *   written in ORIGINAL token order through perm (row perm[j] gets the
+ *   gradient of permuted row j).  Deterministic (no atomics).
+ *   ws: moga_workspace_bytes(MOGA_OP_ATTENTION_BACKWARD, N, M, H, D).
+ */
+int moga_group_attention_backward(const void* Qp, const void* Kp, const void* Vp, const void* dOp,
+                                  const float* lse, const float* delta, const int32_t* cu_seqlens,
+                                  const int32_t* perm, int64_t N, int32_t H, int32_t D, int32_t M,
+                                  float softmax_scale, void* dQ, void* dK, void* dV, void* ws,
+                                  size_t ws_bytes, void* stream);
+
+/*
+ * moga_route_backward -- router gradients from dgate (section "MoGA Router",
+ *   Eq. 3 differentiated with the hard choice held fixed): with p the softmax
+ *   of the recomputed logits r = X W_r^T (+ bias) and g = group_id,
+ *   dlogits[n][j] = dgate[n] * p_g * ([j == g] - p_j), then
+ *   dX = dlogits W_r (float [N, d_model]), dWr = dlogits^T X (float [M, d_model]),
+ *   dbias = sum_n dlogits[n] (float [M]; may be NULL).  Fixed-order
+ *   reductions (bitwise repeatable).  X, Wr bf16 as moga_route; d_model a
+ *   multiple of 32.  ws: moga_workspace_bytes(MOGA_OP_ROUTE_BACKWARD, N, M, 1, d_model).
+ */
+int moga_route_backward(const void* X, const void* Wr, const float* bias, const int32_t* group_id,
+                        const float* dgate, int64_t N, int32_t d_model, int32_t M, float* dX,
+                        float* dWr, float* dbias, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moga_workspace_bytes -- bytes of workspace `op` needs for these sizes

@@ -7,7 +7,9 @@ the library has not been built (`python sparse_attention_long_router_amd/build.p
 
 from ._lib import (MOGA_OP_BALANCE_STATS, MOGA_OP_GROUP_ATTENTION, MOGA_OP_PERMUTE,  # noqa: F401
                    MOGA_OP_ROUTE, MOGA_OP_STGA_ATTENTION, MOGA_OP_UNPERMUTE, LIB_PATH, MogaError, version)
-from .binding import (MogaForward, moga_balance_stats, moga_group_attention,  # noqa: F401
+from .binding import (MogaForward, MogaTraining, moga_balance_stats, moga_group_attention,  # noqa: F401
+                      moga_group_attention_backward, moga_group_attention_train, moga_route_backward,
+                      moga_unpermute_backward,
                       moga_group_attention_fused, moga_group_attention_unpermute, moga_permute, moga_route,
                       moga_stga_attention, moga_stga_shot_attention, moga_stga_shot_workspace_bytes, moga_unpermute,
                       moga_workspace_bytes)

@@ -21,6 +21,8 @@ MOGA_OP_GROUP_ATTENTION = 2
 MOGA_OP_UNPERMUTE = 3
 MOGA_OP_STGA_ATTENTION = 4
 MOGA_OP_BALANCE_STATS = 5
+MOGA_OP_ROUTE_BACKWARD = 6
+MOGA_OP_ATTENTION_BACKWARD = 7
 
 # every symbol include/moga.h declares, with its ctypes signature
 _c = ctypes
@@ -41,6 +43,12 @@ SIGNATURES = {
                                             _i32, _i32, _f32, _f32, _f32, _vp, _vp, _sz, _vp]),
     "moga_stga_shot_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "moga_balance_stats": (_c.c_int, [_vp, _vp, _i64, _i32, _f32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moga_group_attention_train": (_c.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _sz,
+                                              _vp]),
+    "moga_unpermute_backward": (_c.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "moga_group_attention_backward": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
+                                                 _f32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moga_route_backward": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moga_workspace_bytes": (_sz, [_i32, _i64, _i32, _i32, _i32]),
     "moga_strerror": (_c.c_char_p, [_i32]),
     "moga_version": (_i32, []),

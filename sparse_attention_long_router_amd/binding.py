@@ -11,7 +11,8 @@ from __future__ import annotations
 import torch
 
 from . import _lib
-from ._lib import (MOGA_OP_BALANCE_STATS, MOGA_OP_GROUP_ATTENTION, MOGA_OP_PERMUTE, check, ptr, stream_handle)
+from ._lib import (MOGA_OP_ATTENTION_BACKWARD, MOGA_OP_BALANCE_STATS, MOGA_OP_GROUP_ATTENTION, MOGA_OP_PERMUTE,
+                   MOGA_OP_ROUTE_BACKWARD, check, ptr, stream_handle)
 
 BF16 = torch.bfloat16
 
@@ -331,3 +332,145 @@ class MogaForward:
             moga_stga_attention(Q, K, V, g["T"], g["Hs"], g["Ws"], g["win_t"], g["tile_h"], g["tile_w"],
                                 softmax_scale, stga_weight, moga_weight, self.O)
         return self.O
+
+
+# ---------------------------------------------------------------------------
+# Backward pass
+# ---------------------------------------------------------------------------
+
+F32 = torch.float32
+
+
+def moga_group_attention_train(Qp, Kp, Vp, cu_seqlens, softmax_scale=0.0, Op=None, lse=None, ws=None):
+    """moga_group_attention that also returns lse float32 [H, N] (natural-log
+    log-sum-exp of each row's scaled scores, permuted rows)."""
+    _need(Qp, "Qp", BF16, 3)
+    N, H, D = Qp.shape
+    _need(Kp, "Kp", BF16, 3, Qp.shape)
+    _need(Vp, "Vp", BF16, 3, Qp.shape)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    M = cu_seqlens.shape[0] - 1
+    Op = torch.empty_like(Qp) if Op is None else Op
+    lse = torch.empty((H, N), dtype=F32, device=Qp.device) if lse is None else lse
+    _need(Op, "Op", BF16, 3, Qp.shape)
+    _need(lse, "lse", F32, 2, (H, N))
+    ws, nbytes = _workspace(MOGA_OP_GROUP_ATTENTION, N, M, H, D, ws, Qp.device)
+    check(_lib.LIB.moga_group_attention_train(ptr(Qp), ptr(Kp), ptr(Vp), ptr(cu_seqlens), N, H, D, M,
+                                              float(softmax_scale), ptr(Op), ptr(lse), ptr(ws), nbytes,
+                                              stream_handle()),
+          "moga_group_attention_train")
+    return Op, lse
+
+
+def moga_unpermute_backward(dO, Op, perm, gate, dOp=None, delta=None, dgate=None):
+    """(dOp bf16 [N, H, D] permuted, delta float32 [H, N], dgate float32 [N])."""
+    _need(dO, "dO", BF16, 3)
+    N, H, D = dO.shape
+    _need(Op, "Op", BF16, 3, dO.shape)
+    _need(perm, "perm", torch.int32, 1, (N,))
+    _need(gate, "gate", F32, 1, (N,))
+    dOp = torch.empty_like(dO) if dOp is None else dOp
+    delta = torch.empty((H, N), dtype=F32, device=dO.device) if delta is None else delta
+    dgate = torch.empty(N, dtype=F32, device=dO.device) if dgate is None else dgate
+    _need(dOp, "dOp", BF16, 3, dO.shape)
+    _need(delta, "delta", F32, 2, (H, N))
+    _need(dgate, "dgate", F32, 1, (N,))
+    check(_lib.LIB.moga_unpermute_backward(ptr(dO), ptr(Op), ptr(perm), ptr(gate), N, H, D, ptr(dOp), ptr(delta),
+                                           ptr(dgate), stream_handle()),
+          "moga_unpermute_backward")
+    return dOp, delta, dgate
+
+
+def moga_group_attention_backward(Qp, Kp, Vp, dOp, lse, delta, cu_seqlens, perm, softmax_scale=0.0, dQ=None,
+                                  dK=None, dV=None, ws=None):
+    """dQ, dK, dV bf16 [N, H, D] in original token order (through perm)."""
+    _need(Qp, "Qp", BF16, 3)
+    N, H, D = Qp.shape
+    for name, t in (("Kp", Kp), ("Vp", Vp), ("dOp", dOp)):
+        _need(t, name, BF16, 3, Qp.shape)
+    _need(lse, "lse", F32, 2, (H, N))
+    _need(delta, "delta", F32, 2, (H, N))
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _need(perm, "perm", torch.int32, 1, (N,))
+    M = cu_seqlens.shape[0] - 1
+    dQ = torch.empty_like(Qp) if dQ is None else dQ
+    dK = torch.empty_like(Qp) if dK is None else dK
+    dV = torch.empty_like(Qp) if dV is None else dV
+    for name, t in (("dQ", dQ), ("dK", dK), ("dV", dV)):
+        _need(t, name, BF16, 3, Qp.shape)
+    ws, nbytes = _workspace(MOGA_OP_ATTENTION_BACKWARD, N, M, H, D, ws, Qp.device)
+    check(_lib.LIB.moga_group_attention_backward(ptr(Qp), ptr(Kp), ptr(Vp), ptr(dOp), ptr(lse), ptr(delta),
+                                                 ptr(cu_seqlens), ptr(perm), N, H, D, M, float(softmax_scale),
+                                                 ptr(dQ), ptr(dK), ptr(dV), ptr(ws), nbytes, stream_handle()),
+          "moga_group_attention_backward")
+    return dQ, dK, dV
+
+
+def moga_route_backward(X, Wr, group_id, dgate, bias=None, dX=None, dWr=None, dbias=None, ws=None):
+    """Router gradients (dX float32 [N, d_model], dWr float32 [M, d_model],
+    dbias float32 [M]) from dgate."""
+    _need(X, "X", BF16, 2)
+    M, d = Wr.shape
+    _need(Wr, "Wr", BF16, 2, (M, X.shape[1]))
+    N = X.shape[0]
+    _need(group_id, "group_id", torch.int32, 1, (N,))
+    _need(dgate, "dgate", F32, 1, (N,))
+    if bias is not None:
+        _need(bias, "bias", F32, 1, (M,))
+    dX = torch.empty((N, d), dtype=F32, device=X.device) if dX is None else dX
+    dWr = torch.empty((M, d), dtype=F32, device=X.device) if dWr is None else dWr
+    dbias = torch.empty(M, dtype=F32, device=X.device) if dbias is None else dbias
+    _need(dX, "dX", F32, 2, (N, d))
+    _need(dWr, "dWr", F32, 2, (M, d))
+    _need(dbias, "dbias", F32, 1, (M,))
+    ws, nbytes = _workspace(MOGA_OP_ROUTE_BACKWARD, N, M, 1, d, ws, X.device)
+    check(_lib.LIB.moga_route_backward(ptr(X), ptr(Wr), ptr(bias), ptr(group_id), ptr(dgate), N, d, M, ptr(dX),
+                                       ptr(dWr), ptr(dbias), ptr(ws), nbytes, stream_handle()),
+          "moga_route_backward")
+    return dX, dWr, dbias
+
+
+class MogaTraining:
+    """One MoGA layer for training: ``forward`` runs route -> permute (with
+    gathered copies) -> attention that saves Op and lse -> gated unpermute and
+    keeps what the backward needs; ``backward(dO)`` runs the unpermute,
+    attention and router backward and returns the gradients of sum(O * dO)
+    w.r.t. Q, K, V (bf16, original order), the router's share of dX, dWr and
+    dbias (float32), plus dgate.  Buffers are allocated once."""
+
+    def __init__(self, N, d_model, H, D, M, device):
+        self.N, self.d_model, self.H, self.D, self.M = N, d_model, H, D, M
+        e = lambda *s, dt=BF16: torch.empty(*s, dtype=dt, device=device)  # noqa: E731
+        self.group_id, self.gate = e(N, dt=torch.int32), e(N, dt=F32)
+        self.Qp, self.Kp, self.Vp, self.Op, self.O = (e(N, H, D) for _ in range(5))
+        self.lse = e(H, N, dt=F32)
+        self.perm, self.cu_seqlens, self.max_seqlen = e(N, dt=torch.int32), e(M + 1, dt=torch.int32), e(1, dt=torch.int32)
+        self.ws_perm = e(max(moga_workspace_bytes(MOGA_OP_PERMUTE, N, M, H, D), 1), dt=torch.uint8)
+        self.ws_attn = e(max(moga_workspace_bytes(MOGA_OP_GROUP_ATTENTION, N, M, H, D), 1), dt=torch.uint8)
+        self.ws_bwd = e(max(moga_workspace_bytes(MOGA_OP_ATTENTION_BACKWARD, N, M, H, D), 1), dt=torch.uint8)
+        self.ws_rbwd = e(max(moga_workspace_bytes(MOGA_OP_ROUTE_BACKWARD, N, M, 1, d_model), 1), dt=torch.uint8)
+        self.dOp, self.delta, self.dgate = e(N, H, D), e(H, N, dt=F32), e(N, dt=F32)
+        self.dQ, self.dK, self.dV = (e(N, H, D) for _ in range(3))
+        self.dX, self.dWr, self.dbias = e(N, d_model, dt=F32), e(M, d_model, dt=F32), e(M, dt=F32)
+        self.saved = None
+
+    def forward(self, X, Wr, Q, K, V, bias=None, softmax_scale=0.0):
+        moga_route(X, Wr, bias, self.group_id, self.gate)
+        moga_permute(self.group_id, self.M, Q, K, V, self.Qp, self.Kp, self.Vp, self.perm, self.cu_seqlens,
+                     self.max_seqlen, self.ws_perm)
+        moga_group_attention_train(self.Qp, self.Kp, self.Vp, self.cu_seqlens, softmax_scale, self.Op, self.lse,
+                                   self.ws_attn)
+        moga_unpermute(self.Op, self.perm, self.gate, 0.0, self.O)
+        self.saved = (X, Wr, bias, softmax_scale)
+        return self.O
+
+    def backward(self, dO):
+        if self.saved is None:
+            raise RuntimeError("backward before forward")
+        X, Wr, bias, softmax_scale = self.saved
+        moga_unpermute_backward(dO, self.Op, self.perm, self.gate, self.dOp, self.delta, self.dgate)
+        moga_group_attention_backward(self.Qp, self.Kp, self.Vp, self.dOp, self.lse, self.delta, self.cu_seqlens,
+                                      self.perm, softmax_scale, self.dQ, self.dK, self.dV, self.ws_bwd)
+        moga_route_backward(X, Wr, self.group_id, self.dgate, bias, self.dX, self.dWr, self.dbias, self.ws_rbwd)
+        return {"dQ": self.dQ, "dK": self.dK, "dV": self.dV, "dX": self.dX, "dWr": self.dWr, "dbias": self.dbias,
+                "dgate": self.dgate}

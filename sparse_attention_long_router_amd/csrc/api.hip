@@ -4,7 +4,6 @@
 extern "C" size_t moga_workspace_bytes(int32_t op, int64_t N, int32_t M, int32_t H, int32_t D) {
   using namespace moga;
   (void)H;
-  (void)D;
   if (N < 1 || N >= (int64_t(1) << 31) || M < 1 || M > kMaxGroups) return 0;
   switch (op) {
     case MOGA_OP_PERMUTE:  // per-(group, block) counts and base offsets
@@ -13,6 +12,13 @@ extern "C" size_t moga_workspace_bytes(int32_t op, int64_t N, int32_t M, int32_t
       return align_up(sizeof(AttnSchedule), 256);
     case MOGA_OP_BALANCE_STATS:  // per-(group, block) counts and gate sums
       return align_up(2 * (size_t)M * (size_t)sort_blocks(N) * 4, 256);
+    case MOGA_OP_ATTENTION_BACKWARD:  // two largest-group-first schedules (key and query tiles)
+      return 2048;
+    case MOGA_OP_ROUTE_BACKWARD: {  // dlogits [N, M], dW_r block partials, db block partials
+      if (D < 1) return 0;
+      const size_t nblk = (size_t)ceil_div(N, 1024);
+      return align_up((size_t)N * M * 4, 256) + align_up(nblk * M * (size_t)D * 4, 256) + align_up(nblk * M * 4, 256);
+    }
     default:
       return 0;
   }

@@ -462,11 +462,15 @@ __device__ __forceinline__ void tile_max(const uint16_t* Ks, int k0, int len, co
 //               (the gated unpermute fused into the attention)
 //   kEpiGatedInPlace: the row already is the original token n (gather on
 //               load); O[n] = gate[n] * attn + beta * O[n]
-enum { kEpiPlain = 0, kEpiScaled = 1, kEpiGated = 2, kEpiGatedInPlace = 3 };
+//   kEpiPlainLse: as kEpiPlain, and lse[head][row] = log sum_j exp(scale s_j)
+//               (natural log) for the backward pass
+enum { kEpiPlain = 0, kEpiScaled = 1, kEpiGated = 2, kEpiGatedInPlace = 3, kEpiPlainLse = 4 };
 struct Epilogue {
   float alpha, beta;
   const int32_t* perm;
   const float* gate;
+  float* lse;        // kEpiPlainLse: [H][n_rows]
+  int64_t n_rows;
 };
 
 template <int D, int QB, class Rows, int kEpi>
@@ -618,8 +622,13 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave) void attn_kernel(
   // ---- normalise and store: reg r of block db is channel 32*db + 8*(r/4) + 4*hh + r%4
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
-    const float inv = 1.0f / halves_sum(rs[b].l);
+    const float lsum = halves_sum(rs[b].l);
+    const float inv = 1.0f / lsum;
     if (!qvalid[b]) continue;
+    if constexpr (kEpi == kEpiPlainLse) {
+      // log2 of the denominator plus the exponent offset, in natural units
+      if (hh == 0) epi.lse[(int64_t)w.head * epi.n_rows + qrow[b]] = (rs[b].m_ref + __log2f(lsum)) * 0.6931471805599453f;
+    }
     float scale = inv, keep = 0.f;
     int64_t orow = qrow[b];
     if constexpr (kEpi == kEpiScaled) {
@@ -767,7 +776,7 @@ extern "C" int moga_group_attention(const void* Qp, const void* Kp, const void* 
   MOGA_LAUNCH_CHECK();
   MogaRows rows{cu_seqlens, sched, M, H};
   const int64_t bound = (ceil_div(N, kBM) + M) * H;
-  const Epilogue epi{1.f, 0.f, nullptr, nullptr};
+  const Epilogue epi{1.f, 0.f, nullptr, nullptr, nullptr, 0};
   if (D == 128) return launch_attn<128, MogaRows, kEpiPlain>(Qp, Kp, Vp, Op, (int64_t)H * D, scale, epi, rows, bound, st);
   return launch_attn<64, MogaRows, kEpiPlain>(Qp, Kp, Vp, Op, (int64_t)H * D, scale, epi, rows, bound, st);
 }
@@ -789,7 +798,7 @@ extern "C" int moga_stga_attention(const void* Q, const void* K, const void* V, 
   if (items > 0x7fffffff) return MOGA_ERR_SHAPE;
   StgaRows rows{Hs, Ws, win_t, tile_h, tile_w, Hs / tile_h, Ws / tile_w, tpg, H, (int)items};
   hipStream_t st = as_stream(stream);
-  const Epilogue epi{alpha, beta, nullptr, nullptr};
+  const Epilogue epi{alpha, beta, nullptr, nullptr, nullptr, 0};
   if (D == 128) return launch_attn<128, StgaRows, kEpiScaled>(Q, K, V, O, (int64_t)H * D, scale, epi, rows, items, st);
   return launch_attn<64, StgaRows, kEpiScaled>(Q, K, V, O, (int64_t)H * D, scale, epi, rows, items, st);
 }
@@ -811,7 +820,7 @@ extern "C" int moga_group_attention_unpermute(const void* Qp, const void* Kp, co
   MOGA_LAUNCH_CHECK();
   MogaRows rows{cu_seqlens, sched, M, H};
   const int64_t bound = (ceil_div(N, kBM) + M) * H;
-  const Epilogue epi{1.f, beta, perm, gate};
+  const Epilogue epi{1.f, beta, perm, gate, nullptr, 0};
   if (D == 128) return launch_attn<128, MogaRows, kEpiGated>(Qp, Kp, Vp, O, (int64_t)H * D, scale, epi, rows, bound, st);
   return launch_attn<64, MogaRows, kEpiGated>(Qp, Kp, Vp, O, (int64_t)H * D, scale, epi, rows, bound, st);
 }
@@ -851,7 +860,7 @@ extern "C" int moga_stga_shot_attention(const void* Q, const void* K, const void
   shot_windows_kernel<<<1, kShotThreads, 0, st>>>(shot_start, n_shots, T, win_t, augment, max_windows, win, nwin);
   MOGA_LAUNCH_CHECK();
   ShotRows rows{win, nwin, Hs, Ws, tile_h, tile_w, ntx, nspatial, tpg, H};
-  const Epilogue epi{alpha, beta, nullptr, nullptr};
+  const Epilogue epi{alpha, beta, nullptr, nullptr, nullptr, 0};
   if (D == 128) return launch_attn<128, ShotRows, kEpiScaled>(Q, K, V, O, (int64_t)H * D, scale, epi, rows, items, st);
   return launch_attn<64, ShotRows, kEpiScaled>(Q, K, V, O, (int64_t)H * D, scale, epi, rows, items, st);
 }
@@ -873,8 +882,29 @@ extern "C" int moga_group_attention_fused(const void* Q, const void* K, const vo
   MOGA_LAUNCH_CHECK();
   MogaPermRows rows{MogaRows{cu_seqlens, sched, M, H}, perm};
   const int64_t bound = (ceil_div(N, kBM) + M) * H;
-  const Epilogue epi{1.f, beta, nullptr, gate};
+  const Epilogue epi{1.f, beta, nullptr, gate, nullptr, 0};
   if (D == 128)
     return launch_attn<128, MogaPermRows, kEpiGatedInPlace>(Q, K, V, O, (int64_t)H * D, scale, epi, rows, bound, st);
   return launch_attn<64, MogaPermRows, kEpiGatedInPlace>(Q, K, V, O, (int64_t)H * D, scale, epi, rows, bound, st);
+}
+
+extern "C" int moga_group_attention_train(const void* Qp, const void* Kp, const void* Vp, const int32_t* cu_seqlens,
+                                          int64_t N, int32_t H, int32_t D, int32_t M, float softmax_scale, void* Op,
+                                          float* lse, void* ws, size_t ws_bytes, void* stream) {
+  using namespace moga;
+  if (!Qp || !Kp || !Vp || !cu_seqlens || !Op || !lse) return MOGA_ERR_NULL;
+  if (N < 1 || N >= (int64_t(1) << 31) || M < 1 || H < 1 || D < 1) return MOGA_ERR_SHAPE;
+  if (M > kMaxGroups || !valid_head_dims(H, D)) return MOGA_ERR_UNSUPPORTED;
+  const size_t need = moga_workspace_bytes(MOGA_OP_GROUP_ATTENTION, N, M, H, D);
+  if (!ws || ws_bytes < need) return MOGA_ERR_WORKSPACE;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
+  hipStream_t st = as_stream(stream);
+  auto* sched = static_cast<AttnSchedule*>(ws);
+  schedule_kernel<<<1, kWave, 0, st>>>(cu_seqlens, M, H, sched);
+  MOGA_LAUNCH_CHECK();
+  MogaRows rows{cu_seqlens, sched, M, H};
+  const int64_t bound = (ceil_div(N, kBM) + M) * H;
+  const Epilogue epi{1.f, 0.f, nullptr, nullptr, lse, N};
+  if (D == 128) return launch_attn<128, MogaRows, kEpiPlainLse>(Qp, Kp, Vp, Op, (int64_t)H * D, scale, epi, rows, bound, st);
+  return launch_attn<64, MogaRows, kEpiPlainLse>(Qp, Kp, Vp, Op, (int64_t)H * D, scale, epi, rows, bound, st);
 }

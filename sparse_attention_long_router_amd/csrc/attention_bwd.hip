@@ -1,0 +1,422 @@
+// Backward of the group attention for gfx950 (learned groups, permuted rows).
+// Page "MoGA: Mixture-of-Groups Attention for End-to-End Long Video
+// Generation": Eq. 1 restricted to a group (the MoGA output equation,
+// "Grouped Attention"), differentiated with the softmax saved as its
+// per-row log-sum-exp.  For a group and head, with c = scale:
+//   P = exp(c Q K^T - lse),  dV = P^T dA,  dP = dA V^T,
+//   dS = P * (dP - delta),   dQ = c dS K,  dK = c dS^T Q,
+// where dA is the gated upstream gradient in permuted order and delta the
+// row sums of dA * A (both from moga_unpermute_backward).
+//
+// Two kernels, no atomics (results are bitwise repeatable):
+//   dkdv_kernel: K and V rows of 32 keys per wave stay in registers as MFMA
+//     operands; the group's queries stream through LDS in tiles of 64 (Q, dA,
+//     lse, delta).  S = Q K^T puts one key per lane, so P and dS feed
+//     dV^T += dA^T P and dK^T += Q^T dS directly as MFMA B operands, with
+//     dA^T and Q^T read from LDS by transposing reads.
+//   dq_kernel: Q and dA rows of 32 queries per wave stay in registers; keys
+//     and values stream through LDS as in the forward pass.  S^T = K Q^T and
+//     dP^T = V dA^T put one query per lane, and dQ^T += K^T dS^T.
+// Rows past a group's end are read as zeros through the buffer range check:
+// a zero query row has a zero upstream gradient and a zero key row a zero
+// operand, so they add nothing to the rows that are stored, and the exact
+// P = exp(s - lse) needs no normaliser.  The dq kernel still gives the zero
+// key rows of a group's last tile no weight, so that a very negative
+// log-sum-exp cannot turn them into inf * 0.
+#include "moga_internal.h"
+
+typedef int32_t i32x4v __attribute__((ext_vector_type(4)));
+__device__ void raw_buffer_load_lds(i32x4v rsrc, __attribute__((address_space(3))) void* lds, int size, int voffset,
+                                    int soffset, int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+namespace moga {
+namespace {
+
+constexpr int kTile = 64;      // rows per streamed LDS tile
+constexpr int kDqBM = 256;     // queries per dq work item (8 waves x 32)
+constexpr int kDqWaves = 8;
+constexpr int kDkvBN = 128;    // keys per dkdv work item (4 waves x 32)
+constexpr int kDkvWaves = 4;
+constexpr int kRun = 8;        // consecutive items per XCD
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16-byte chunk swizzles (cpr = chunks per row): kRowsOnly keeps row reads
+// conflict-free; kBoth keeps both row reads and transposing reads free of
+// bank conflicts (distinct chunks for any 8 consecutive rows, and for the 4
+// rows x 2 chunks of one transposing read group).
+enum { kRowsOnly = 0, kBoth = 1 };
+template <int kSwz>
+__device__ __forceinline__ int swz(int r, int cpr) {
+  if constexpr (kSwz == kRowsOnly) return r & (cpr - 1);
+  return cpr == 16 ? (((r & 3) << 2) | ((r >> 2) & 3)) : (((r & 3) << 1) | ((r >> 2) & 1));
+}
+
+__device__ __forceinline__ i32x4v row_rsrc(const uint16_t* base, int64_t n_rows, int64_t row_bytes, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  int64_t range = n_rows > 0 ? (n_rows - 1) * row_bytes + bytes : 0;
+  range = range < 0xffffffffll ? range : 0xffffffffll;
+  i32x4v r;
+  r[0] = (int32_t)(uint32_t)a;
+  r[1] = (int32_t)(uint32_t)(a >> 32);
+  r[2] = (int32_t)(uint32_t)range;
+  r[3] = 0x00020000;
+  return r;
+}
+
+// kTile rows of one head (row stride row_stride elements) into LDS, swizzled.
+template <int D, int NW, int kSwz>
+__device__ __forceinline__ void load_tile(i32x4v rs, uint16_t* T, int64_t row_stride, int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int LOADS = kTile * CPR / (NW * kWave);
+  static_assert(LOADS >= 1 && kTile * CPR == LOADS * NW * kWave, "tile must split evenly over the waves");
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) {
+    const int q = (wave * LOADS + j) * kWave + lane;
+    const int r = q / CPR, p = q % CPR;
+    const int lds_off = (wave * LOADS + j) * kWave * 8;
+    raw_buffer_load_lds(rs, (lds_void*)(T + lds_off), 16, r * (int)row_stride * 2 + ((p ^ swz<kSwz>(r, CPR)) << 4),
+                        0, 0, 0);
+  }
+}
+
+// A from 32 LDS rows (rbase..rbase+31), B from registers: C[m = row][n = lane % 32].
+// Reg r of the result is row 8*(r/4) + 4*hh + r%4 of the block.
+template <int D, int kSwz>
+__device__ __forceinline__ f32x16 rows_mma(const uint16_t* T, int rbase, const bf16x8 (&b)[D / 16], int lane) {
+  constexpr int CPR = D / 8;
+  const int hh = lane >> 5, row = rbase + (lane & 31);
+  bf16x8 a[D / 16];
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st)
+    a[st] = *reinterpret_cast<const bf16x8*>(T + row * D + ((2 * st + hh) ^ swz<kSwz>(row, CPR)) * 8);
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16 c = {};
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[st], b[st], c, 0, 0, 0);
+  return c;
+}
+
+// acc[db] (C = T^T block: 32 channels x 32 columns) += T[rows]^T * p over the
+// 32 LDS rows rbase..rbase+31, with A = T^T from transposing reads and
+// B = p, whose k-slots follow the C layout of rows_mma (reg 8t + j of the
+// half is row 16t + 8*(j/4) + 4*hh + j%4).
+template <int D, int kSwz>
+__device__ __forceinline__ void tr_mma(const uint16_t* T, int rbase, const bf16x8 (&p)[2], int lane,
+                                       f32x16 (&acc)[D / 32]) {
+  constexpr int CPR = D / 8;
+  const int hh = lane >> 5;
+  const int tr_r = (lane & 15) >> 2, tr_q = lane & 3, tr_g = (lane >> 4) & 1;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int r1 = rbase + 16 * t + 4 * hh + tr_r;
+    const int r2 = r1 + 8;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int col = 32 * db + 16 * tr_g + 4 * tr_q;
+      const int ch = col >> 3, within = col & 7;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(T + r1 * D + ((ch ^ swz<kSwz>(r1, CPR)) << 3) + within));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(T + r2 * D + ((ch ^ swz<kSwz>(r2, CPR)) << 3) + within));
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[t], acc[db], 0, 0, 0);
+    }
+  }
+}
+
+// MFMA B-operand fragments of one row (lane % 32 picks the row, lane / 32 the
+// 8-channel half of each 16-channel step); zeros past n_rows.
+template <int D>
+__device__ __forceinline__ void load_frags(const uint16_t* __restrict__ base, int64_t row_stride, int row, int n_rows,
+                                           int lane, bf16x8 (&f)[D / 16]) {
+  const int hh = lane >> 5;
+  if (row < n_rows) {
+    const uint16_t* p = base + (int64_t)row * row_stride + 8 * hh;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) f[st] = *reinterpret_cast<const bf16x8*>(p + 16 * st);
+  } else {
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) f[st] = bf16x8{};
+  }
+}
+
+// Store a C-layout accumulator (lane = row of the output, reg r of block db =
+// channel 32*db + 8*(r/4) + 4*hh + r%4) times s as bf16 to out[orow].
+template <int D>
+__device__ __forceinline__ void store_rows(uint16_t* __restrict__ out, const f32x16 (&acc)[D / 32], float s, int hh) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d0 = 32 * db + 8 * q4 + 4 * hh;
+      const u32x2 pk = {pack_bf16x2(acc[db][4 * q4] * s, acc[db][4 * q4 + 1] * s),
+                        pack_bf16x2(acc[db][4 * q4 + 2] * s, acc[db][4 * q4 + 3] * s)};
+      *reinterpret_cast<u32x2*>(out + d0) = pk;
+    }
+}
+
+struct Item {
+  int len;     // group size
+  int t0;      // first row (group-local) of this item
+  int head;
+  int row0;    // first permuted row of the group
+};
+
+__device__ __forceinline__ bool decode(const AttnSchedule* sched, const int32_t* cu, int M, int tile, int item,
+                                       Item& w) {
+  if (item >= sched->prefix[M]) return false;
+  int i = 0;
+  while (i + 1 < M && sched->prefix[i + 1] <= item) ++i;
+  const int g = sched->order[i];
+  const int local = item - sched->prefix[i];
+  w.row0 = cu[g];
+  w.len = cu[g + 1] - w.row0;
+  const int nt = (w.len + tile - 1) / tile;
+  w.head = local / nt;
+  w.t0 = (local - w.head * nt) * tile;
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: 4 waves x 32 keys, queries streamed in tiles of 64
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kDkvWaves * kWave) void dkdv_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dA, const float* __restrict__ lse, const float* __restrict__ delta,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ perm, const AttnSchedule* __restrict__ sched, int M,
+    int64_t N, int64_t row_stride, float scale, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV) {
+  constexpr int DBLK = D / 32;
+  constexpr int NW = kDkvWaves;
+  __shared__ __attribute__((aligned(1024))) uint16_t Qs[2][kTile * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t As[2][kTile * D];
+  __shared__ __attribute__((aligned(256))) float Ls[2][kTile];
+  __shared__ __attribute__((aligned(256))) float Ds[2][kTile];
+
+  Item w;
+  if (!decode(sched, cu, M, kDkvBN, xcd_remap(blockIdx.x, kRun), w)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
+  const int64_t hoff = (int64_t)w.head * D;
+  const int ntiles = (w.len + kTile - 1) / kTile;
+  const float c2 = scale * 1.4426950408889634f;  // scores to log2 units
+
+  // tile t: Q and dA rows, lse and delta of queries t*64 .. t*64+63
+  auto issue = [&](int buf, int t) {
+    const int64_t first = (int64_t)w.row0 + (int64_t)t * kTile;
+    const int64_t n = w.len - (int64_t)t * kTile;
+    load_tile<D, NW, kBoth>(row_rsrc(Q + first * row_stride + hoff, n, row_stride * 2, D * 2), Qs[buf], row_stride,
+                            wave, lane);
+    load_tile<D, NW, kBoth>(row_rsrc(dA + first * row_stride + hoff, n, row_stride * 2, D * 2), As[buf], row_stride,
+                            wave, lane);
+    if (wave == 0) {
+      const float* lp = lse + (int64_t)w.head * N + first;
+      const float* dp = delta + (int64_t)w.head * N + first;
+      raw_buffer_load_lds(row_rsrc(reinterpret_cast<const uint16_t*>(lp), n, 4, 4), (lds_void*)Ls[buf], 4, lane * 4,
+                          0, 0, 0);
+      raw_buffer_load_lds(row_rsrc(reinterpret_cast<const uint16_t*>(dp), n, 4, 4), (lds_void*)Ds[buf], 4, lane * 4,
+                          0, 0, 0);
+    }
+  };
+  issue(0, 0);
+
+  // this wave's 32 keys as B operands (zeros past the group end)
+  const int key = w.t0 + wave * 32 + (lane & 31);
+  bf16x8 kf[D / 16], vf[D / 16];
+  load_frags<D>(K + (int64_t)w.row0 * row_stride + hoff, row_stride, key, w.len, lane, kf);
+  load_frags<D>(V + (int64_t)w.row0 * row_stride + hoff, row_stride, key, w.len, lane, vf);
+
+  f32x16 dk[DBLK], dv[DBLK];
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db) {
+    dk[db] = f32x16{};
+    dv[db] = f32x16{};
+  }
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t + 1 < ntiles) issue(buf ^ 1, t + 1);
+    const uint16_t* Qt = Qs[buf];
+    const uint16_t* At = As[buf];
+#pragma unroll
+    for (int qb = 0; qb < kTile / 32; ++qb) {
+      const f32x16 s = rows_mma<D, kBoth>(Qt, qb * 32, kf, lane);   // S[query][key]
+      const f32x16 dp = rows_mma<D, kBoth>(At, qb * 32, vf, lane);  // dP[query][key]
+      bf16x8 pb[2], sb[2];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {  // rows qb*32 + 8g + 4hh + 0..3
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Ls[buf][qb * 32 + 8 * g + 4 * hh]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Ds[buf][qb * 32 + 8 * g + 4 * hh]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * g + i;
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l4[i] * 1.4426950408889634f));
+          pb[r >> 3][r & 7] = (__bf16)p;
+          sb[r >> 3][r & 7] = (__bf16)(p * (dp[r] - d4[i]));
+        }
+      }
+      tr_mma<D, kBoth>(At, qb * 32, pb, lane, dv);  // dV^T += dA^T P
+      tr_mma<D, kBoth>(Qt, qb * 32, sb, lane, dk);  // dK^T += Q^T dS
+    }
+  }
+
+  if (key < w.len) {
+    const int64_t orow = perm[w.row0 + key];
+    store_rows<D>(dK + orow * row_stride + hoff, dk, scale, hh);
+    store_rows<D>(dV + orow * row_stride + hoff, dv, 1.0f, hh);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: 8 waves x 32 queries, keys and values streamed in tiles of 64
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kDqWaves * kWave) void dq_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dA, const float* __restrict__ lse, const float* __restrict__ delta,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ perm, const AttnSchedule* __restrict__ sched, int M,
+    int64_t N, int64_t row_stride, float scale, uint16_t* __restrict__ dQ) {
+  constexpr int DBLK = D / 32;
+  constexpr int NW = kDqWaves;
+  __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][kTile * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][kTile * D];
+
+  Item w;
+  if (!decode(sched, cu, M, kDqBM, xcd_remap(blockIdx.x, kRun), w)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
+  const int64_t hoff = (int64_t)w.head * D;
+  const int ntiles = (w.len + kTile - 1) / kTile;
+  const float c2 = scale * 1.4426950408889634f;
+
+  auto issue = [&](int buf, int t) {
+    const int64_t first = (int64_t)w.row0 + (int64_t)t * kTile;
+    const int64_t n = w.len - (int64_t)t * kTile;
+    load_tile<D, NW, kBoth>(row_rsrc(K + first * row_stride + hoff, n, row_stride * 2, D * 2), Ks[buf], row_stride,
+                            wave, lane);
+    load_tile<D, NW, kRowsOnly>(row_rsrc(V + first * row_stride + hoff, n, row_stride * 2, D * 2), Vs[buf],
+                                row_stride, wave, lane);
+  };
+  issue(0, 0);
+
+  const int qi = w.t0 + wave * 32 + (lane & 31);
+  bf16x8 qf[D / 16], af[D / 16];
+  load_frags<D>(Q + (int64_t)w.row0 * row_stride + hoff, row_stride, qi, w.len, lane, qf);
+  load_frags<D>(dA + (int64_t)w.row0 * row_stride + hoff, row_stride, qi, w.len, lane, af);
+  const bool qvalid = qi < w.len;
+  const float l2 = qvalid ? lse[(int64_t)w.head * N + w.row0 + qi] * 1.4426950408889634f : 0.f;
+  const float dl = qvalid ? delta[(int64_t)w.head * N + w.row0 + qi] : 0.f;
+
+  f32x16 dq[DBLK];
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db) dq[db] = f32x16{};
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t + 1 < ntiles) issue(buf ^ 1, t + 1);
+#pragma unroll
+    for (int kb = 0; kb < kTile / 32; ++kb) {
+      const f32x16 s = rows_mma<D, kBoth>(Ks[buf], kb * 32, qf, lane);        // S^T[key][query]
+      const f32x16 dp = rows_mma<D, kRowsOnly>(Vs[buf], kb * 32, af, lane);   // dP^T[key][query]
+      bf16x8 sb[2];
+      // keys past the group end (zero rows, last tile only) get no weight
+      const int kend = t + 1 < ntiles ? kTile : w.len - t * kTile;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kk = kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        const float p = kk < kend ? __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l2)) : 0.f;
+        sb[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dl));
+      }
+      tr_mma<D, kBoth>(Ks[buf], kb * 32, sb, lane, dq);  // dQ^T += K^T dS^T
+    }
+  }
+
+  if (qvalid) store_rows<D>(dQ + (int64_t)perm[w.row0 + qi] * row_stride + hoff, dq, scale, hh);
+}
+
+// Groups by decreasing size and the prefix count of (head, tile) items.
+__global__ __launch_bounds__(kWave) void bwd_schedule_kernel(const int32_t* __restrict__ cu, int M, int H, int tile,
+                                                           AttnSchedule* __restrict__ sched) {
+  __shared__ int order_s[kMaxGroups];
+  const int g = threadIdx.x;
+  const int n = g < M ? cu[g + 1] - cu[g] : -1;
+  if (g < M) {
+    int rank = 0;
+    for (int o = 0; o < M; ++o) {
+      const int no = cu[o + 1] - cu[o];
+      rank += (no > n) || (no == n && o < g);
+    }
+    order_s[rank] = g;
+  }
+  __syncthreads();
+  int items = 0;
+  if (g < M) {
+    const int og = order_s[g];
+    sched->order[g] = og;
+    items = (cu[og + 1] - cu[og] + tile - 1) / tile * H;
+  }
+  int incl = items;
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int v = __shfl_up(incl, off);
+    if (g >= off) incl += v;
+  }
+  if (g < M) sched->prefix[g + 1] = incl;
+  if (g == 0) sched->prefix[0] = 0;
+}
+
+int64_t grid_for(int64_t items) {
+  const int64_t run = (int64_t)kNumXcd * kRun;
+  return ceil_div(items, run) * run;
+}
+
+template <int D>
+int launch_bwd(const uint16_t* Qp, const uint16_t* Kp, const uint16_t* Vp, const uint16_t* dAp, const float* lse,
+               const float* delta, const int32_t* cu, const int32_t* perm, AttnSchedule* sk, AttnSchedule* sq, int M,
+               int64_t N, int H, float scale, uint16_t* dQ, uint16_t* dK, uint16_t* dV, hipStream_t st) {
+  const int64_t rs = (int64_t)H * D;
+  const int64_t gk = grid_for((ceil_div(N, kDkvBN) + M) * H);
+  const int64_t gq = grid_for((ceil_div(N, kDqBM) + M) * H);
+  if (gk > 0x7fffffff || gq > 0x7fffffff) return MOGA_ERR_SHAPE;
+  dkdv_kernel<D><<<dim3((unsigned)gk), kDkvWaves * kWave, 0, st>>>(Qp, Kp, Vp, dAp, lse, delta, cu, perm, sk, M, N,
+                                                                    rs, scale, dK, dV);
+  MOGA_LAUNCH_CHECK();
+  dq_kernel<D><<<dim3((unsigned)gq), kDqWaves * kWave, 0, st>>>(Qp, Kp, Vp, dAp, lse, delta, cu, perm, sq, M, N, rs,
+                                                                 scale, dQ);
+  MOGA_LAUNCH_CHECK();
+  return MOGA_OK;
+}
+
+}  // namespace
+}  // namespace moga
+
+extern "C" int moga_group_attention_backward(const void* Qp, const void* Kp, const void* Vp, const void* dOp,
+                                             const float* lse, const float* delta, const int32_t* cu_seqlens,
+                                             const int32_t* perm, int64_t N, int32_t H, int32_t D, int32_t M,
+                                             float softmax_scale, void* dQ, void* dK, void* dV, void* ws,
+                                             size_t ws_bytes, void* stream) {
+  using namespace moga;
+  if (!Qp || !Kp || !Vp || !dOp || !lse || !delta || !cu_seqlens || !perm || !dQ || !dK || !dV) return MOGA_ERR_NULL;
+  if (N < 1 || N >= (int64_t(1) << 31) || M < 1 || H < 1 || D < 1) return MOGA_ERR_SHAPE;
+  if (M > kMaxGroups || !valid_head_dims(H, D)) return MOGA_ERR_UNSUPPORTED;
+  const size_t need = moga_workspace_bytes(MOGA_OP_ATTENTION_BACKWARD, N, M, H, D);
+  if (!ws || ws_bytes < need) return MOGA_ERR_WORKSPACE;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
+  hipStream_t st = as_stream(stream);
+  auto* sk = static_cast<AttnSchedule*>(ws);
+  auto* sq = reinterpret_cast<AttnSchedule*>(static_cast<char*>(ws) + 1024);
+  bwd_schedule_kernel<<<1, kWave, 0, st>>>(cu_seqlens, M, H, kDkvBN, sk);
+  MOGA_LAUNCH_CHECK();
+  bwd_schedule_kernel<<<1, kWave, 0, st>>>(cu_seqlens, M, H, kDqBM, sq);
+  MOGA_LAUNCH_CHECK();
+  auto c = [](const void* p) { return static_cast<const uint16_t*>(p); };
+  auto m = [](void* p) { return static_cast<uint16_t*>(p); };
+  if (D == 128)
+    return launch_bwd<128>(c(Qp), c(Kp), c(Vp), c(dOp), lse, delta, cu_seqlens, perm, sk, sq, M, N, H, scale, m(dQ),
+                           m(dK), m(dV), st);
+  return launch_bwd<64>(c(Qp), c(Kp), c(Vp), c(dOp), lse, delta, cu_seqlens, perm, sk, sq, M, N, H, scale, m(dQ),
+                        m(dK), m(dV), st);
+}

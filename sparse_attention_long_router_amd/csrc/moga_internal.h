@@ -68,3 +68,8 @@ inline bool valid_head_dims(int32_t H, int32_t D) {
   return H >= 1 && (D == 64 || D == 128) && (int64_t)H * D <= 8192;
 }
 }  // namespace moga
+
+// Router-logit gradient from the route kernel (route.hip), used by
+// moga_route_backward: dlogits [N, M] float.
+int moga_route_dlogits(const uint16_t* x, const uint16_t* w, const float* bias, int64_t N, int32_t d_model, int32_t M,
+                       const int32_t* group_id, const float* dgate, float* dlogits, hipStream_t st);

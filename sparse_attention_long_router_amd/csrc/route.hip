@@ -26,10 +26,15 @@ constexpr int kRouteWaves = 4;
 constexpr int kRouteTokBlocks = 4;  // 16-token blocks per wave
 constexpr int kRouteTokensPerBlock = kRouteWaves * kRouteTokBlocks * 16;  // 256
 
-template <int MB>  // ceil(M / 16) group blocks
+// kGrad = false: group_id and gate out.  kGrad = true (backward): group_id
+// and dgate in, and the router-logit gradient out,
+//   dlogits[t][j] = dgate[t] * p_g * ([j == g] - p_j),  p = softmax(r_t),
+// the derivative of the gate p_g (Eq. 3) with the hard choice g held fixed.
+template <int MB, bool kGrad>  // ceil(M / 16) group blocks
 __global__ __launch_bounds__(kRouteWaves * kWave) void route_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wr, const float* __restrict__ bias,
-    int64_t N, int dm, int M, int32_t* __restrict__ group_id, float* __restrict__ gate) {
+    int64_t N, int dm, int M, int32_t* __restrict__ group_id, float* __restrict__ gate,
+    const float* __restrict__ dgate, float* __restrict__ dlogits) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int q = lane >> 4, c = lane & 15;
   const int64_t tok0 = (int64_t)blockIdx.x * kRouteTokensPerBlock + wave * (kRouteTokBlocks * 16);
@@ -139,18 +144,44 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void route_kernel(
     s += __shfl_xor(s, 16);
     s += __shfl_xor(s, 32);
     const int64_t t = tok0 + tb * 16 + c;
-    if (q == 0 && t < N) {
-      group_id[t] = besti;
-      gate[t] = 1.0f / s;
+    if constexpr (!kGrad) {
+      if (q == 0 && t < N) {
+        group_id[t] = besti;
+        gate[t] = 1.0f / s;
+      }
+    } else {
+      const int64_t tc = t < N ? t : N - 1;
+      const int g = group_id[tc];
+      const float inv = 1.0f / s;
+      float pg = 0.f;  // p of the chosen group, gathered from the lane quad that holds it
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (mb * 16 + q * 4 + i == g) pg = expf(r[mb][i] - best) * inv;
+      pg += __shfl_xor(pg, 16);
+      pg += __shfl_xor(pg, 32);
+      const float f = dgate[tc] * pg;
+      if (t < N) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = mb * 16 + q * 4 + i;
+            if (j < M) dlogits[t * M + j] = f * ((j == g ? 1.f : 0.f) - expf(r[mb][i] - best) * inv);
+          }
+      }
     }
   }
 }
 
-template <int MB>
+template <int MB, bool kGrad = false>
 void launch_route(const uint16_t* X, const uint16_t* Wr, const float* bias, int64_t N, int dm, int M,
-                  int32_t* gid, float* gate, hipStream_t st) {
+                  int32_t* gid, float* gate, hipStream_t st, const float* dgate = nullptr,
+                  float* dlogits = nullptr) {
   const int64_t blocks = ceil_div(N, kRouteTokensPerBlock);
-  route_kernel<MB><<<dim3((unsigned)blocks), dim3(kRouteWaves * kWave), 0, st>>>(X, Wr, bias, N, dm, M, gid, gate);
+  route_kernel<MB, kGrad><<<dim3((unsigned)blocks), dim3(kRouteWaves * kWave), 0, st>>>(X, Wr, bias, N, dm, M, gid,
+                                                                                       gate, dgate, dlogits);
 }
 
 }  // namespace
@@ -170,6 +201,22 @@ extern "C" int moga_route(const void* X, const void* Wr, const float* bias, int6
     case 2: launch_route<2>(x, w, bias, N, d_model, M, group_id, gate, st); break;
     case 3: launch_route<3>(x, w, bias, N, d_model, M, group_id, gate, st); break;
     default: launch_route<4>(x, w, bias, N, d_model, M, group_id, gate, st); break;
+  }
+  MOGA_LAUNCH_CHECK();
+  return MOGA_OK;
+}
+
+// Router-logit gradient (backward of the gate); internal entry used by
+// moga_route_backward.
+int moga_route_dlogits(const uint16_t* x, const uint16_t* w, const float* bias, int64_t N, int32_t d_model, int32_t M,
+                       const int32_t* group_id, const float* dgate, float* dlogits, hipStream_t st) {
+  using namespace moga;
+  int32_t* gid = const_cast<int32_t*>(group_id);  // read only when kGrad
+  switch ((M + 15) / 16) {
+    case 1: launch_route<1, true>(x, w, bias, N, d_model, M, gid, nullptr, st, dgate, dlogits); break;
+    case 2: launch_route<2, true>(x, w, bias, N, d_model, M, gid, nullptr, st, dgate, dlogits); break;
+    case 3: launch_route<3, true>(x, w, bias, N, d_model, M, gid, nullptr, st, dgate, dlogits); break;
+    default: launch_route<4, true>(x, w, bias, N, d_model, M, gid, nullptr, st, dgate, dlogits); break;
   }
   MOGA_LAUNCH_CHECK();
   return MOGA_OK;

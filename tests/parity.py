@@ -13,6 +13,13 @@ MEAN_ABS = 2e-3
 REL_FRO = 1e-2
 GATE_RTOL = 1e-4  # float32 gate; derivation in DESIGN.md ("Tolerances")
 
+# Gradients (backward pass): bf16 operands P, dS and the gated upstream
+# gradient each carry a 2^-9 relative rounding, accumulated in float32, and
+# bf16 outputs round once more; gradients have no fixed scale (dK grows with
+# the group), so both bars are relative to the reference.
+GRAD_REL_FRO = 1e-2
+GRAD_REL_MAX = 2e-2
+
 
 def output_errors(got, want):
     got = np.asarray(got, dtype=np.float64)
@@ -35,6 +42,20 @@ def output_ok(e):
 def assert_output_close(got, want, what="O"):
     e = output_errors(got, want)
     assert output_ok(e), f"{what}: {e} exceeds max_abs {MAX_ABS} / mean_abs {MEAN_ABS} / rel_fro {REL_FRO}"
+    return e
+
+
+GRAD_ATOL = 1e-5  # float32 noise floor for gradients whose exact value is 0
+
+
+def assert_grad_close(got, want, what="grad"):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    e = output_errors(got, want)
+    peak = max(float(np.abs(want).max()) if want.size else 0.0, 1e-30)
+    e["rel_max"] = e["max_abs"] / peak
+    ok = e["finite"] and (e["max_abs"] <= GRAD_ATOL or (e["rel_fro"] <= GRAD_REL_FRO and e["rel_max"] <= GRAD_REL_MAX))
+    assert ok, f"{what}: {e} exceeds rel_fro {GRAD_REL_FRO} / rel_max {GRAD_REL_MAX} (floor {GRAD_ATOL})"
     return e
 
 

@@ -33,7 +33,7 @@ def declared_symbols():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 13, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(lib, n), n
     from sparse_attention_long_router_amd import _lib
@@ -182,3 +182,32 @@ def test_stga_shot_workspace_and_argument_errors(lib):
     assert s(*aug) == ESHAPE                    # negative augmentation
     assert s(*args(ws=None)) == EWS
     assert s(*args(wsb=need - 1)) == EWS
+
+
+def test_backward_workspace_and_argument_errors(lib):
+    ws = lib.moga_workspace_bytes
+    assert ws(7, 1000, 4, 2, 128) >= 2 * (64 + 65) * 4
+    n = ws(6, 190320, 16, 1, 1536)
+    assert n >= 190320 * 16 * 4 + 186 * 16 * 1536 * 4 and n % 256 == 0
+    assert ws(6, 1000, 4, 1, 0) == 0
+    t = lib.moga_group_attention_train
+    nb = ws(2, 100, 4, 2, 128)
+    assert t(FAKE, FAKE, FAKE, FAKE, 100, 2, 128, 4, 0.0, FAKE, None, FAKE, nb, None) == ENULL   # lse
+    assert t(FAKE, FAKE, FAKE, FAKE, 100, 2, 96, 4, 0.0, FAKE, FAKE, FAKE, nb, None) == EUNSUP
+    assert t(FAKE, FAKE, FAKE, FAKE, 100, 2, 128, 4, 0.0, FAKE, FAKE, FAKE, nb - 1, None) == EWS
+    u = lib.moga_unpermute_backward
+    assert u(FAKE, FAKE, FAKE, FAKE, 100, 2, 128, FAKE, FAKE, None, None) == ENULL
+    assert u(FAKE, FAKE, FAKE, FAKE, 0, 2, 128, FAKE, FAKE, FAKE, None) == ESHAPE
+    assert u(FAKE, FAKE, FAKE, FAKE, 100, 2, 32, FAKE, FAKE, FAKE, None) == EUNSUP
+    b = lib.moga_group_attention_backward
+    nbb = ws(7, 100, 4, 2, 128)
+    args = [FAKE] * 8 + [100, 2, 128, 4, 0.0, FAKE, FAKE, FAKE, FAKE, nbb, None]
+    assert b(*args[:4], None, *args[5:]) == ENULL            # lse
+    assert b(*args[:8], 0, *args[9:]) == ESHAPE
+    assert b(*args[:11], 65, *args[12:]) == EUNSUP
+    assert b(*args[:17], nbb - 1, None) == EWS
+    r = lib.moga_route_backward
+    nr = ws(6, 100, 4, 1, 128)
+    assert r(FAKE, FAKE, None, FAKE, None, 100, 128, 4, FAKE, FAKE, None, FAKE, nr, None) == ENULL   # dgate
+    assert r(FAKE, FAKE, None, FAKE, FAKE, 100, 100, 4, FAKE, FAKE, None, FAKE, nr, None) == EUNSUP  # d % 32
+    assert r(FAKE, FAKE, None, FAKE, FAKE, 100, 128, 4, FAKE, FAKE, None, FAKE, nr - 1, None) == EWS
