@@ -46,6 +46,7 @@ def parse():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--path", default="fused_epilogue", choices=["fused_epilogue", "gather_on_load", "separate"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass timing")
     ap.add_argument("--cpu-rows", type=int, default=2000, help="sampled query rows per group for the oracle")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of MIB MiB (reference for HBM byte counters)")
@@ -126,6 +127,44 @@ def cpu_baseline(inp, wl, counts, rows_per_group):
                    f"({t_attn:.2f} s, {sample_flops / 1e9:.1f} GFLOP), extrapolated by FLOPs to the full step "
                    f"({t_full:.1f} s); float64 NumPy, {len(os.sched_getaffinity(0))} cores visible"),
     }
+
+
+def backward_timing(moga, wl, X, Wr, Q, K, V, flops_fwd, steps):
+    """The training backward of the MoGA layer (unpermute, attention and
+    router backward) on the same inputs, after a training forward.  The
+    attention's algorithmic work is 2.5x the forward's (five n^2 D products
+    per group and head: S, dP, dV, dQ, dK)."""
+    import torch
+
+    tr = moga.MogaTraining(wl.N, wl.d_model, wl.H, wl.D, wl.M, X.device)
+    g = torch.Generator(device=X.device).manual_seed(wl.seed)
+    dO = torch.randn(Q.shape, generator=g, device=X.device).bfloat16()
+    tr.forward(X, Wr, Q, K, V)
+    tr.backward(dO)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for e in evs:
+        e[0].record(stream)
+        moga.moga_unpermute_backward(dO, tr.Op, tr.perm, tr.gate, tr.dOp, tr.delta, tr.dgate)
+        e[1].record(stream)
+        moga.moga_group_attention_backward(tr.Qp, tr.Kp, tr.Vp, tr.dOp, tr.lse, tr.delta, tr.cu_seqlens, tr.perm, 0.0,
+                                           tr.dQ, tr.dK, tr.dV, tr.ws_bwd)
+        e[2].record(stream)
+        moga.moga_route_backward(X, Wr, tr.group_id, tr.dgate, None, tr.dX, tr.dWr, tr.dbias, tr.ws_rbwd)
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    names = ["unpermute_backward", "group_attention_backward", "route_backward"]
+    ms = {n: sum(e[k].elapsed_time(e[k + 1]) for e in evs) / steps for k, n in enumerate(names)}
+    total = sum(ms.values())
+    attn = ms["group_attention_backward"]
+    del tr
+    return {"ms": round(total, 4), "breakdown_ms": {k: round(v, 4) for k, v in ms.items()}, "steps": steps,
+            "attention_tflops": round(2.5 * flops_fwd / (attn * 1e-3) / 1e12, 2),
+            "attention_mfma_frac": round(2.5 * flops_fwd / (attn * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "flops_per_launch": 2.5 * flops_fwd,
+            "unpermute_backward_gbs": round(wl.N * (6 * wl.H * wl.D + 4 * wl.H + 12) / (ms["unpermute_backward"] * 1e-3)
+                                            / 1e9, 1)}
 
 
 def main():
@@ -250,6 +289,9 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if not args.no_backward:
+        del fwd  # free the forward buffers before the training ones
+        out["backward"] = backward_timing(moga, wl, X, Wr, Q, K, V, flops_moga, steps=max(2, args.steps // 4))
     hbm = {"route": wl.N * (2 * wl.d_model + 8) + 2 * wl.M * wl.d_model}  # algorithmic bytes per launch
     if args.path != "gather_on_load":  # sort + gather; the sort alone is latency-bound (reported in ms only)
         hbm["permute"] = wl.N * (12 * wl.H * wl.D + 16)
