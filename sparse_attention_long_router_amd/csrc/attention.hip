@@ -54,6 +54,7 @@ template <int QB>
 constexpr int waves_for() { return kBM / (32 * QB); }
 constexpr int kBN = 64;                             // keys per LDS tile
 constexpr int kXcdRun = 8;                          // consecutive items per XCD
+constexpr int kTabKeys = 8192;                      // key-row table entries (index-map windows)
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -71,6 +72,7 @@ struct Work {
 struct MogaRows {
   static constexpr bool kIndirect = false;
   static constexpr bool kContiguous = true;  // key row i of a group is row0 + i
+  static constexpr bool kTable = false;
   const int32_t* cu;
   const AttnSchedule* sched;
   int M, H;
@@ -101,6 +103,7 @@ struct MogaRows {
 struct MogaPermRows {
   static constexpr bool kIndirect = true;
   static constexpr bool kContiguous = false;
+  static constexpr bool kTable = false;
   MogaRows base;
   const int32_t* perm;
   __device__ __forceinline__ bool decode(int item, Work& w) const { return base.decode(item, w); }
@@ -112,6 +115,7 @@ struct MogaPermRows {
 struct StgaRows {
   static constexpr bool kIndirect = false;
   static constexpr bool kContiguous = false;
+  static constexpr bool kTable = true;  // key rows tabulated in LDS once per item
   int Hs, Ws, win_t, tile_h, tile_w, nty, ntx, tiles_per_group, H, items;
   __device__ __forceinline__ bool decode(int item, Work& w) const {
     if (item >= items) return false;
@@ -157,6 +161,7 @@ struct ShotWindow {
 struct ShotRows {
   static constexpr bool kIndirect = false;
   static constexpr bool kContiguous = false;
+  static constexpr bool kTable = true;
   const ShotWindow* win;
   const int* nwin;
   int Hs, Ws, tile_h, tile_w, ntx, nspatial, tpg, H;
@@ -256,6 +261,30 @@ __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ K, const
     key = key < w.len ? key : w.len - 1;
     const int64_t base = rows.key(w, key) * row_stride + hoff;
     const int lds_off = (wave * LOADS + j) * kWave * 8;  // uint16 elements, wave-uniform
+    __builtin_amdgcn_global_load_lds((global_void*)(K + base + (p ^ kswz(r, CPR)) * 8), (lds_void*)(Ks + lds_off),
+                                     16, 0, 0);
+    __builtin_amdgcn_global_load_lds((global_void*)(V + base + (p ^ vswz(r, CPR)) * 8), (lds_void*)(Vs + lds_off),
+                                     16, 0, 0);
+  }
+}
+
+// Table variant of issue_tile for index-map windows: the token row of every
+// key was written to LDS (tab) once per work item, so the per-tile issue reads
+// it instead of evaluating the (t, y, x) map per 16-byte chunk.
+template <int D, int NW>
+__device__ __forceinline__ void issue_tile_tab(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                                               uint16_t* Ks, uint16_t* Vs, const int32_t* tab, int len,
+                                               int64_t row_stride, int64_t hoff, int k0, int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int LOADS = kBN * CPR / (NW * kWave);
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) {
+    const int q = (wave * LOADS + j) * kWave + lane;
+    const int r = q / CPR, p = q % CPR;
+    int key = k0 + r;
+    key = key < len ? key : len - 1;
+    const int64_t base = (int64_t)tab[key] * row_stride + hoff;
+    const int lds_off = (wave * LOADS + j) * kWave * 8;
     __builtin_amdgcn_global_load_lds((global_void*)(K + base + (p ^ kswz(r, CPR)) * 8), (lds_void*)(Ks + lds_off),
                                      16, 0, 0);
     __builtin_amdgcn_global_load_lds((global_void*)(V + base + (p ^ vswz(r, CPR)) * 8), (lds_void*)(Vs + lds_off),
@@ -494,6 +523,16 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave) void attn_kernel(
   const int nfull = w.len / kBN;            // tiles without a group end inside
   const int ntiles = (w.len + kBN - 1) / kBN;
 
+  // Index-map windows: tabulate every key's token row once (up to kTabKeys).
+  __shared__ int32_t ktab[Rows::kTable ? kTabKeys : 1];
+  [[maybe_unused]] const bool use_tab = Rows::kTable && w.len <= kTabKeys;  // uniform per block
+  if constexpr (Rows::kTable) {
+    if (use_tab) {
+      for (int i = tid; i < w.len; i += NW * kWave) ktab[i] = (int32_t)rows.key(w, i);
+      __syncthreads();
+    }
+  }
+
   // Tile t's K/V loads; with gather on load, also fetch tile t+1's key rows.
   [[maybe_unused]] int32_t kidx[tile_loads<D, NW>()];
   auto issue = [&](uint16_t* Kd, uint16_t* Vd, int t) {
@@ -505,6 +544,8 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave) void attn_kernel(
     } else if constexpr (Rows::kIndirect) {
       issue_tile_idx<D, NW>(K, V, Kd, Vd, kidx, row_stride, hoff, wave, lane);
       if (t + 1 < ntiles) fetch_keys<D, NW>(rows, w, (t + 1) * kBN, wave, lane, kidx);
+    } else if (use_tab) {
+      issue_tile_tab<D, NW>(K, V, Kd, Vd, ktab, w.len, row_stride, hoff, t * kBN, wave, lane);
     } else {
       issue_tile<D, NW>(K, V, Kd, Vd, rows, w, row_stride, hoff, t * kBN, wave, lane);
     }
@@ -525,6 +566,10 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave) void attn_kernel(
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) qf[b][s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
   }
+
+  // A wave whose queries all lie past the group end (the last query tile of a
+  // group) computes nothing, freeing its SIMD for the wave that shares it.
+  const bool wave_live = w.q0 + wave * QB * 32 < w.nq;  // uniform per wave
 
   f32x16 o[QB][DBLK];
   RowState rs[QB];
@@ -551,6 +596,7 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave) void attn_kernel(
     for (int b = 0; b < QB; ++b) mx[b] = -INFINITY;
     auto step = [&](const uint16_t* Ks, const uint16_t* Vs, int t, auto mask) {
       constexpr bool kMask = decltype(mask)::value;
+      if (!wave_live) return;  // keeps its barriers and loads, skips the math
       if constexpr (kMax)
         tile_max<D, QB, kMask>(Ks, t * kBN, w.len, qf, mx, lane);
       else
@@ -585,6 +631,8 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave) void attn_kernel(
   {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  }
+  if (wave_live) {
     f32x16 s[QB];
     qk_half<D, QB>(Ks0, qf, 0, lane, s);
     if (w.len < 32) mask_half<true, QB>(s, 0, w.len, hh);
