@@ -171,8 +171,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not supported. "
-              "Multi-GPU sharding is described in DESIGN.md, not implemented.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} (WORLD_SIZE={world}) is not supported: "
+              "sharding the layer across GPUs (by head) is not implemented.", file=sys.stderr)
         sys.exit(2)
 
     if args.calibrate_copy:

@@ -19,7 +19,7 @@ exception is the router's argmax, which is taken on the float32 rounding of
 the exact float64 logits, because that is the precision the GPU kernel decides
 in; inputs are generated so that the top-1 margin is far above that rounding.
 
-Readings of points the pages leave open (each is listed in the design doc):
+Readings of points the pages leave open:
   * softmax scale is 1/sqrt(D) with D the per-head dimension;
   * group ids are 0-based; argmax ties go to the lowest index;
   * inside a group, tokens keep their original order (stable permutation);

@@ -5,8 +5,8 @@ tokens (480x832 video, VAE (4,8,8) and patchify (1,2,2), "Vanilla
 Self-Attention" section of the MoGA explainer page), Wan2.1-1.3B attention
 (d_model 1536, 12 heads of 128) and Wan2.1-14B attention (d_model 5120, 40
 heads of 128), with 30-second (~190k tokens) and minute-scale (~580k tokens)
-contexts.  Group counts, the mixture recipe and the STGA tile come from the
-workload definitions recorded in the design doc.
+contexts.  Group counts, the mixture recipe and the STGA tile are those of the
+workload definitions below.
 """
 
 from __future__ import annotations

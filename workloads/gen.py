@@ -1,6 +1,6 @@
 """Seeded synthetic inputs for the MoGA forward hot path (torch, any device).
 
-Recipe (stated in DESIGN.md, "Input recipe"):
+Recipe:
   * W_r ~ N(0, 1/d_model) with shape [M, d_model]; W_q, W_k, W_v ~ N(0, 1/d_model)
     with shape [d_model, H*D].
   * Tokens: "none" -> x ~ N(0, I).  Mixtures -> x_n = gamma * w_hat[pi(k_n)]
