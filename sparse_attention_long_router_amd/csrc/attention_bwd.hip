@@ -10,8 +10,8 @@
 //
 // Two kernels, no atomics (results are bitwise repeatable):
 //   dkdv_kernel: K and V rows of 32 keys per wave stay in registers as MFMA
-//     operands; the group's queries stream through LDS in tiles of 64 (Q, dA,
-//     lse, delta).  S = Q K^T puts one key per lane, so P and dS feed
+//     operands; the group's queries stream through LDS in tiles of 128 (Q,
+//     dA, lse, delta).  S = Q K^T puts one key per lane, so P and dS feed
 //     dV^T += dA^T P and dK^T += Q^T dS directly as MFMA B operands, with
 //     dA^T and Q^T read from LDS by transposing reads.
 //   dq_kernel: Q and dA rows of 32 queries per wave stay in registers; keys
@@ -32,7 +32,8 @@ __device__ void raw_buffer_load_lds(i32x4v rsrc, __attribute__((address_space(3)
 namespace moga {
 namespace {
 
-constexpr int kTile = 64;      // rows per streamed LDS tile
+constexpr int kTileQ = 128;    // query rows per streamed LDS tile (dkdv_kernel)
+constexpr int kTileK = 128;    // key rows per streamed LDS tile (dq_kernel)
 constexpr int kDqBM = 256;     // queries per dq work item (8 waves x 32)
 constexpr int kDqWaves = 8;
 constexpr int kDkvBN = 128;    // keys per dkdv work item (4 waves x 32)
@@ -66,7 +67,7 @@ __device__ __forceinline__ i32x4v row_rsrc(const uint16_t* base, int64_t n_rows,
 }
 
 // kTile rows of one head (row stride row_stride elements) into LDS, swizzled.
-template <int D, int NW, int kSwz>
+template <int D, int NW, int kSwz, int kTile>
 __device__ __forceinline__ void load_tile(i32x4v rs, uint16_t* T, int64_t row_stride, int wave, int lane) {
   constexpr int CPR = D / 8;
   constexpr int LOADS = kTile * CPR / (NW * kWave);
@@ -190,6 +191,7 @@ __global__ __launch_bounds__(kDkvWaves * kWave) void dkdv_kernel(
     int64_t N, int64_t row_stride, float scale, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV) {
   constexpr int DBLK = D / 32;
   constexpr int NW = kDkvWaves;
+  constexpr int kTile = kTileQ;
   __shared__ __attribute__((aligned(1024))) uint16_t Qs[2][kTile * D];
   __shared__ __attribute__((aligned(1024))) uint16_t As[2][kTile * D];
   __shared__ __attribute__((aligned(256))) float Ls[2][kTile];
@@ -206,17 +208,18 @@ __global__ __launch_bounds__(kDkvWaves * kWave) void dkdv_kernel(
   auto issue = [&](int buf, int t) {
     const int64_t first = (int64_t)w.row0 + (int64_t)t * kTile;
     const int64_t n = w.len - (int64_t)t * kTile;
-    load_tile<D, NW, kBoth>(row_rsrc(Q + first * row_stride + hoff, n, row_stride * 2, D * 2), Qs[buf], row_stride,
+    load_tile<D, NW, kBoth, kTile>(row_rsrc(Q + first * row_stride + hoff, n, row_stride * 2, D * 2), Qs[buf], row_stride,
                             wave, lane);
-    load_tile<D, NW, kBoth>(row_rsrc(dA + first * row_stride + hoff, n, row_stride * 2, D * 2), As[buf], row_stride,
+    load_tile<D, NW, kBoth, kTile>(row_rsrc(dA + first * row_stride + hoff, n, row_stride * 2, D * 2), As[buf], row_stride,
                             wave, lane);
-    if (wave == 0) {
-      const float* lp = lse + (int64_t)w.head * N + first;
-      const float* dp = delta + (int64_t)w.head * N + first;
-      raw_buffer_load_lds(row_rsrc(reinterpret_cast<const uint16_t*>(lp), n, 4, 4), (lds_void*)Ls[buf], 4, lane * 4,
-                          0, 0, 0);
-      raw_buffer_load_lds(row_rsrc(reinterpret_cast<const uint16_t*>(dp), n, 4, 4), (lds_void*)Ds[buf], 4, lane * 4,
-                          0, 0, 0);
+    if (wave < kTile / kWave) {  // 64 entries per wave; past the group end the range is empty
+      const int o = wave * kWave;
+      const float* lp = lse + (int64_t)w.head * N + first + o;
+      const float* dp = delta + (int64_t)w.head * N + first + o;
+      raw_buffer_load_lds(row_rsrc(reinterpret_cast<const uint16_t*>(lp), n - o, 4, 4), (lds_void*)(Ls[buf] + o), 4,
+                          lane * 4, 0, 0, 0);
+      raw_buffer_load_lds(row_rsrc(reinterpret_cast<const uint16_t*>(dp), n - o, 4, 4), (lds_void*)(Ds[buf] + o), 4,
+                          lane * 4, 0, 0, 0);
     }
   };
   issue(0, 0);
@@ -281,6 +284,7 @@ __global__ __launch_bounds__(kDqWaves * kWave) void dq_kernel(
     int64_t N, int64_t row_stride, float scale, uint16_t* __restrict__ dQ) {
   constexpr int DBLK = D / 32;
   constexpr int NW = kDqWaves;
+  constexpr int kTile = kTileK;
   __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][kTile * D];
   __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][kTile * D];
 
@@ -294,9 +298,9 @@ __global__ __launch_bounds__(kDqWaves * kWave) void dq_kernel(
   auto issue = [&](int buf, int t) {
     const int64_t first = (int64_t)w.row0 + (int64_t)t * kTile;
     const int64_t n = w.len - (int64_t)t * kTile;
-    load_tile<D, NW, kBoth>(row_rsrc(K + first * row_stride + hoff, n, row_stride * 2, D * 2), Ks[buf], row_stride,
+    load_tile<D, NW, kBoth, kTile>(row_rsrc(K + first * row_stride + hoff, n, row_stride * 2, D * 2), Ks[buf], row_stride,
                             wave, lane);
-    load_tile<D, NW, kRowsOnly>(row_rsrc(V + first * row_stride + hoff, n, row_stride * 2, D * 2), Vs[buf],
+    load_tile<D, NW, kRowsOnly, kTile>(row_rsrc(V + first * row_stride + hoff, n, row_stride * 2, D * 2), Vs[buf],
                                 row_stride, wave, lane);
   };
   issue(0, 0);
