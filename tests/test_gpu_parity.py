@@ -152,6 +152,7 @@ def test_unpermute_accumulate(moga):
     (6, 6, 10, 3, 3, 5, 2, 128, 1.0, 0.0),     # groups of 45: one partial tile
     (4, 30, 52, 2, 30, 26, 1, 128, 0.5, 0.5),  # Wan-like frames, groups of 1560
     (3, 8, 8, 1, 8, 8, 2, 64, 1.0, 1.0),
+    (6, 30, 52, 6, 30, 52, 1, 64, 1.0, 0.0),     # 9,360-key window: past the key-row table
 ])
 def test_stga(moga, T, Hs, Ws, win_t, th, tw, H, D, alpha, beta):
     N = T * Hs * Ws
@@ -174,6 +175,7 @@ def test_stga(moga, T, Hs, Ws, win_t, th, tw, H, D, alpha, beta):
     (5, 4, 8, [0, 1, 2, 3, 4, 5], 4, 2, 4, 1, 2, 128, 1.0, 0.0),  # every frame its own shot
     (12, 6, 10, [0, 1, 5, 6, 12], 3, 6, 5, 2, 2, 128, 1.0, 0.0),  # two frames per side, clipped
     (10, 30, 52, [0, 4, 10], 3, 30, 26, 3, 1, 128, 1.0, 0.0),   # three per side, Wan-like tile
+    (12, 30, 52, [0, 5, 12], 5, 30, 52, 1, 1, 64, 1.0, 0.0),    # 10,920-key windows: past the table
 ])
 def test_stga_shot(moga, T, Hs, Ws, shots, win_t, th, tw, aug, H, D, alpha, beta):
     N = T * Hs * Ws
