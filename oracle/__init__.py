@@ -26,6 +26,7 @@ from .moga_oracle import (  # noqa: F401
     moga_output_rows,
     balance_stats,
     moga_backward,
+    moga_backward_rows,
     shot_windows,
     stga_shot_attention,
     stga_shot_attention_rows,

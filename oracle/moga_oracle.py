@@ -57,6 +57,7 @@ __all__ = [
     "moga_output_rows",
     "balance_stats",
     "moga_backward",
+    "moga_backward_rows",
     "shot_windows",
     "stga_shot_attention",
     "stga_shot_attention_rows",
@@ -506,3 +507,43 @@ def moga_backward(X, Wr, Q, K, V, M: int, dO, scale=None, bias=None):
     return {"dQ": dQ, "dK": dK, "dV": dV, "dX": dr @ _f64(Wr), "dWr": dr.T @ X, "dbias": dr.sum(axis=0),
             "dgate": dgate, "dlogits": dr, "group_id": g.astype(np.int32), "gate": p, "perm": perm,
             "cu_seqlens": cu, "Op": Op, "lse": lse, "delta": delta}
+
+
+def moga_backward_rows(X, Wr, Q, K, V, M: int, dO, rows, scale=None, bias=None, routed=None):
+    """The per-token gradients of moga_backward for selected ORIGINAL rows
+    only, each from its own group (the same chain rule, the selected queries
+    of a group at a time): dQ[rows] (float64 [len, H, D]), dgate[rows] and
+    the router's dX[rows].  ``routed`` may pass a precomputed
+    (group_id, logits) pair."""
+    X, Wr, dO = _f64(X), _f64(Wr), _f64(dO)
+    N, H, D = Q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    if routed is None:
+        r = router_logits(X, Wr, bias)
+        g = np.argmax(r.astype(np.float32), axis=1)
+    else:
+        g, r = routed
+        r = _f64(r)
+    rows = np.asarray(rows, dtype=np.int64)
+    e = np.exp(r[rows] - r[rows].max(axis=1, keepdims=True))
+    prob = e / e.sum(axis=1, keepdims=True)
+    pg = prob[np.arange(rows.size), g[rows]]
+    dQ = np.zeros((rows.size, H, D))
+    dgate = np.zeros(rows.size)
+    for grp in np.unique(g[rows]):
+        sel = np.nonzero(g[rows] == grp)[0]
+        members = np.nonzero(g == grp)[0]
+        for h in range(H):
+            q, k, v = _f64(Q[rows[sel], h]), _f64(K[members, h]), _f64(V[members, h])
+            S = scale * (q @ k.T)
+            P = np.exp(S - S.max(axis=1, keepdims=True))
+            P /= P.sum(axis=1, keepdims=True)
+            A = P @ v
+            dA = pg[sel, None] * dO[rows[sel], h]
+            dgate[sel] += np.sum(dO[rows[sel], h] * A, axis=1)
+            dS = P * (dA @ v.T - np.sum(dA * A, axis=1, keepdims=True))
+            dQ[sel, h] = scale * (dS @ k)
+    onehot = np.zeros((rows.size, M))
+    onehot[np.arange(rows.size), g[rows]] = 1.0
+    dX = ((dgate * pg)[:, None] * (onehot - prob)) @ Wr
+    return {"dQ": dQ, "dgate": dgate, "dX": dX}

@@ -103,3 +103,46 @@ def test_backward_deterministic(moga):
     torch.cuda.synchronize()
     for k in a:
         assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("name", ["wan13b_21f", "clip30s_122f"])
+def test_backward_full_size(moga, name):
+    """Full-size training backward in the configuration the bench times:
+    sampled rows of dQ, dgate and the router's dX against the oracle row by
+    row, and two group invariants over every row: a group's dV sums to its
+    gated upstream gradient (softmax rows sum to 1) and its dK sums to zero
+    (the row sums of dS vanish)."""
+    from workloads import sample_rows
+    wl = get_workload(name)
+    print(f"[backward] full size {name} N={wl.N} H={wl.H} M={wl.M}", flush=True)
+    inp = make_inputs(wl, device=DEV)
+    X, Wr, Q, K, V = (inp[k] for k in ("X", "Wr", "Q", "K", "V"))
+    g = torch.Generator(device=DEV).manual_seed(wl.seed)
+    dO = torch.randn(Q.shape, generator=g, device=DEV).bfloat16()
+    tr = moga.MogaTraining(wl.N, wl.d_model, wl.H, wl.D, wl.M, DEV)
+    tr.forward(X, Wr, Q, K, V)
+    grads = tr.backward(dO)
+    torch.cuda.synchronize()
+    Xn, Wn = _np(X), _np(Wr)
+    g_ref, _, logits = oracle.route(Xn, Wn)
+    np.testing.assert_array_equal(tr.group_id.cpu().numpy(), g_ref)
+    rows = sample_rows(g_ref, wl.M, per_group=2, seed=wl.seed)
+    ref = oracle.moga_backward_rows(Xn, Wn, _np(Q), _np(K), _np(V), wl.M, _np(dO), rows, routed=(g_ref, logits))
+    idx = torch.from_numpy(rows).to(DEV)
+    errs = {}
+    for k in ("dQ", "dgate", "dX"):
+        errs[k] = round(assert_grad_close(grads[k][idx].float().cpu().numpy(), ref[k], f"{name} {k}")["rel_fro"], 5)
+    # group sums over all rows, in float64 on the device
+    gid = tr.group_id.long()
+    dA = tr.gate[:, None, None].double() * dO.double()
+    sums = {}
+    for k, t in (("dV", grads["dV"].double()), ("dK", grads["dK"].double()), ("dA", dA)):
+        z = torch.zeros((wl.M,) + tuple(Q.shape[1:]), dtype=torch.float64, device=DEV)
+        sums[k] = z.index_add_(0, gid, t).cpu().numpy()
+    absum = {k: torch.zeros((wl.M,) + tuple(Q.shape[1:]), dtype=torch.float64, device=DEV)
+             .index_add_(0, gid, grads[k].double().abs()).cpu().numpy() for k in ("dV", "dK")}
+    v_err = np.abs(sums["dV"] - sums["dA"]).max() / absum["dV"].max()
+    k_err = np.abs(sums["dK"]).max() / absum["dK"].max()
+    print(f"[backward] full size {name}: {rows.size} rows rel_fro {errs}; group-sum errors dV {v_err:.2e} "
+          f"dK {k_err:.2e}", flush=True)
+    assert v_err <= 5e-3 and k_err <= 5e-3

@@ -448,6 +448,30 @@ def test_backward_matches_autograd():
     check_backward_autograd(seed=31, bias=False)
 
 
+def test_backward_rows_match_full_backward():
+    X, Wr, Q, K, V, b = _random_case(39, N=70, d=16, M=3, H=2, D=8, bias=True)
+    dO = _rng(40).standard_normal(Q.shape)
+    full = oracle.moga_backward(X, Wr, Q, K, V, 3, dO, bias=b)
+    rows = np.array([0, 5, 33, 69])
+    part = oracle.moga_backward_rows(X, Wr, Q, K, V, 3, dO, rows, bias=b)
+    for k in ("dQ", "dgate", "dX"):
+        np.testing.assert_allclose(part[k], full[k][rows], rtol=1e-10, atol=1e-12, err_msg=k)
+
+
+def test_backward_group_sum_invariants():
+    # rows of P sum to 1: a group's dV sums to its gated upstream gradient;
+    # rows of dS sum to 0: a group's dK sums to zero
+    X, Wr, Q, K, V, _ = _random_case(41, N=80, M=4)
+    dO = _rng(42).standard_normal(Q.shape)
+    out = oracle.moga_backward(X, Wr, Q, K, V, 4, dO)
+    g, p = out["group_id"], out["gate"]
+    for i in range(4):
+        m = g == i
+        if m.any():
+            np.testing.assert_allclose(out["dV"][m].sum(axis=0), (p[m, None, None] * dO[m]).sum(axis=0), atol=1e-12)
+            np.testing.assert_allclose(out["dK"][m].sum(axis=0), 0.0, atol=1e-12)
+
+
 def test_backward_single_group_router_gradient_vanishes():
     # M = 1: p == 1 for every token and its derivative is zero
     X, Wr, Q, K, V, _ = _random_case(32, N=40, M=1)
