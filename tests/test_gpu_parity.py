@@ -85,6 +85,7 @@ def test_tiny_workload(moga):
     (1, 3, 128, 4),         # a single token
     (5, 2, 64, 3),          # fewer tokens than a tile
     (4097, 3, 128, 16),
+    (700, 64, 128, 4),      # H * D = 8192, the widest supported token row
 ])
 def test_shapes(moga, N, H, D, M):
     _full_check(moga, _inputs("wan13b_21f", N=N, H=H, D=D, M=M, d_model=256), label=f"shape{N}")
@@ -303,3 +304,35 @@ def test_balance_stats(moga, name, M):
     np.testing.assert_allclose(P.cpu().numpy(), Pr, rtol=1e-5, atol=1e-9)
     assert abs(loss.item() - Lr) <= 1e-5 * Lr
     assert torch.equal(P, P2) and torch.equal(loss, loss2)
+
+
+def test_graph_capture_replays(moga):
+    """The whole layer pass (route, permute, attention with the gated
+    unpermute, shot-aware STGA and the per-frame branch) captured once in a
+    HIP graph: every replay, with eager work and synchronisations between
+    them, must equal the eager result bit for bit.  No launch in the pass
+    records a memset, and all scratch is preallocated by MogaForward."""
+    T, Hs, Ws = 6, 6, 10
+    N = T * Hs * Ws
+    inp = _inputs("wan13b_21f", N=N, H=2, D=128, M=5, d_model=128)
+    X, Wr, Q, K, V = (inp[k] for k in ("X", "Wr", "Q", "K", "V"))
+    geo = dict(T=T, Hs=Hs, Ws=Ws, win_t=2, tile_h=3, tile_w=5, shot_start=[0, 2, 3, 6])
+    fwd = moga.MogaForward(N, 128, 2, 128, 5, DEV, stga=geo)
+    eager = fwd(X, Wr, Q, K, V).clone()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fwd(X, Wr, Q, K, V)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = fwd(X, Wr, Q, K, V)
+    for rep in range(3):
+        fwd.O.zero_()
+        junk = (Q.float() * 2).sum()  # unrelated eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep} differs"
+        assert torch.isfinite(junk)
