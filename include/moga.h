@@ -1,5 +1,6 @@
 /*
- * moga.h -- C ABI of the MoGA (Mixture-of-Groups Attention) forward hot path
+ * moga.h -- C ABI of the MoGA (Mixture-of-Groups Attention) forward hot path,
+ * its spatial-temporal group attention branches and its training backward,
  * for AMD Instinct MI355X (gfx950).
  *
  * Source of the operations: the page "MoGA: Mixture-of-Groups Attention for
@@ -101,12 +102,16 @@ int moga_permute(const int32_t* group_id, const void* Q, const void* K, const vo
  * moga_group_attention -- exact softmax attention inside every group
  *   (Eq. 1 restricted to a group; Algorithm 1 step 3), non-causal, each token
  *   attending to itself and every other token of its group, for every head.
+ *   Deterministic: the same inputs give the same bits on every call.
  *   Qp, Kp, Vp  bf16 [N, H, D], rows grouped as described by cu_seqlens
  *   cu_seqlens  int32 [M+1] (device)
  *   softmax_scale  > 0, or <= 0 for 1/sqrt(D)
  *   Op          bf16 [N, H, D] (output, permuted order, no gate)
  *   ws          workspace of at least moga_workspace_bytes(MOGA_OP_GROUP_ATTENTION, N, M, H, D)
- *   bf16 MFMA products, float32 accumulation and online softmax.
+ *   bf16 MFMA products and float32 accumulation; the float32 softmax runs
+ *   against a per-row exponent offset taken from the row's first 32 keys, and
+ *   a work item whose later scores would overflow it is recomputed with its
+ *   exact row maxima, so the result is the exact softmax for any finite input.
  */
 int moga_group_attention(const void* Qp, const void* Kp, const void* Vp,
                          const int32_t* cu_seqlens, int64_t N, int32_t H, int32_t D,

@@ -36,4 +36,5 @@ extern "C" const char* moga_strerror(int32_t status) {
   }
 }
 
-extern "C" int32_t moga_version(void) { return 100; }
+// 0.2.0: shot-aware STGA, gather on load, backward pass
+extern "C" int32_t moga_version(void) { return 200; }
