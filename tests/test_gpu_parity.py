@@ -100,6 +100,30 @@ def test_skewed_with_bias_and_empty_groups(moga):
     assert counts[5] == 0 and counts[2] > 0.5 * 5000
 
 
+@pytest.mark.parametrize("N,d_model,M", [
+    (1000, 32, 5),      # no 128-channel step: the 32-channel tail only
+    (1000, 96, 16),     # tail only, three 32-channel steps
+    (1500, 160, 17),    # one step (no pipeline) + tail; 17..32 groups
+    (2000, 288, 33),    # two steps (drain only) + tail; 33..48 groups
+    (1200, 384, 48),    # three steps: drain with one step left over
+    (3000, 640, 64),    # five steps; 49..64 groups
+    (4098, 1024, 32),   # eight steps: the steady loop runs; ragged token tail
+    (257, 1536, 16),    # one token past the first 256-token block
+])
+def test_route_loop_paths(moga, N, d_model, M):
+    """Router kernel against the oracle over each path of its channel loop
+    (tail only, unpipelined, drain, steady loop) and each group-count class."""
+    inp = _inputs("clip30s_122f", N=N, H=1, D=64, M=M, d_model=d_model, n_components=M)
+    X, Wr = inp["X"], inp["Wr"]
+    bias = torch.linspace(-0.5, 0.5, M, device=DEV) if N % 2 else None
+    print(f"[parity] route N={N} d_model={d_model} M={M} bias={bias is not None}", flush=True)
+    gid, gate = moga.moga_route(X, Wr, bias)
+    torch.cuda.synchronize()
+    g_ref, gate_ref, _ = oracle.route(_np(X), _np(Wr), None if bias is None else bias.cpu().numpy())
+    np.testing.assert_array_equal(gid.cpu().numpy(), g_ref)
+    assert_gate_close(gate.cpu().numpy(), gate_ref)
+
+
 def test_attention_deterministic(moga):
     inp = _inputs("wan13b_21f", N=3000, H=2, D=128, M=4, d_model=256)
     gid, gate = moga.moga_route(inp["X"], inp["Wr"])
