@@ -99,6 +99,23 @@ __device__ __forceinline__ f32x16 rows_mma(const uint16_t* T, int rbase, const b
   return c;
 }
 
+// rows_mma with each A operand read just before its MFMA.  The dq kernel keeps
+// Q and dA fragments and the dQ accumulators live; reading all eight operands
+// ahead costs 32 more VGPRs and spills (measured 40.1 ms against 33.9 ms for
+// the dq kernel at 190k tokens), while the second wave on the SIMD covers the
+// LDS latency this version exposes.
+template <int D, int kSwz>
+__device__ __forceinline__ f32x16 rows_mma_lean(const uint16_t* T, int rbase, const bf16x8 (&b)[D / 16], int lane) {
+  constexpr int CPR = D / 8;
+  const int hh = lane >> 5, row = rbase + (lane & 31);
+  f32x16 c = {};
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st)
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        *reinterpret_cast<const bf16x8*>(T + row * D + ((2 * st + hh) ^ swz<kSwz>(row, CPR)) * 8), b[st], c, 0, 0, 0);
+  return c;
+}
+
 // acc[db] (C = T^T block: 32 channels x 32 columns) += T[rows]^T * p over the
 // 32 LDS rows rbase..rbase+31, with A = T^T from transposing reads and
 // B = p, whose k-slots follow the C layout of rows_mma (reg 8t + j of the
@@ -324,8 +341,16 @@ __global__ __launch_bounds__(kDqWaves * kWave) void dq_kernel(
     if (t + 1 < ntiles) issue(buf ^ 1, t + 1);
 #pragma unroll
     for (int kb = 0; kb < kTile / 32; ++kb) {
-      const f32x16 s = rows_mma<D, kBoth>(Ks[buf], kb * 32, qf, lane);        // S^T[key][query]
-      const f32x16 dp = rows_mma<D, kRowsOnly>(Vs[buf], kb * 32, af, lane);   // dP^T[key][query]
+      // S^T[key][query] and dP^T[key][query]; at D = 64 the preloading form
+      // keeps three waves per SIMD, at D = 128 the lean one avoids spills
+      f32x16 s, dp;
+      if constexpr (D == 128) {
+        s = rows_mma_lean<D, kBoth>(Ks[buf], kb * 32, qf, lane);
+        dp = rows_mma_lean<D, kRowsOnly>(Vs[buf], kb * 32, af, lane);
+      } else {
+        s = rows_mma<D, kBoth>(Ks[buf], kb * 32, qf, lane);
+        dp = rows_mma<D, kRowsOnly>(Vs[buf], kb * 32, af, lane);
+      }
       bf16x8 sb[2];
       // keys past the group end (zero rows, last tile only) get no weight
       const int kend = t + 1 < ntiles ? kTile : w.len - t * kTile;
