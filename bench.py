@@ -5,10 +5,10 @@
 A step is one pass of the whole path over one synthetic batch already resident
 in HBM: route -> permute -> gated group attention (-> STGA sum for workloads
 that have it).  --path picks how attention meets the permutation (default
-fused_epilogue: sort + Q/K/V gather, attention with the gated unpermute in
-its epilogue; gather_on_load: sort only, attention reads Q/K/V rows through
-perm and writes the gated output in place; separate: gather, attention,
-unpermute).
+fused_vt: sort + Q/K gather + V gathered transposed per head, attention with
+the gated unpermute in its epilogue; fused_epilogue: the same with V in row
+layout; gather_on_load: sort only, attention reads Q/K/V rows through perm and
+writes the gated output in place; separate: gather, attention, unpermute).
 Prints ONE JSON line.
 
 value = effective TFLOP/s of the whole step, counting only within-group
@@ -44,7 +44,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--path", default="fused_epilogue", choices=["fused_epilogue", "gather_on_load", "separate"])
+    ap.add_argument("--path", default="fused_vt",
+                    choices=["fused_vt", "fused_epilogue", "gather_on_load", "separate"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass timing")
     ap.add_argument("--cpu-rows", type=int, default=2000, help="sampled query rows per group for the oracle")
@@ -194,6 +195,7 @@ def main():
     stream = torch.cuda.current_stream()
     attn_kernel = {"gather_on_load": "attn_kernel (moga_group_attention_fused)",
                    "fused_epilogue": "attn_kernel (moga_group_attention_unpermute)",
+                   "fused_vt": "attn_kernel (moga_group_attention_unpermute_vt)",
                    "separate": "attn_kernel (moga_group_attention) + unpermute_kernel"}[args.path]
 
     def step(ev=None):
@@ -207,6 +209,9 @@ def main():
         if args.path == "gather_on_load":
             moga.moga_permute(fwd.group_id, wl.M, perm=fwd.perm, cu_seqlens=fwd.cu_seqlens,
                               max_seqlen=fwd.max_seqlen, ws=fwd.ws_perm)
+        elif args.path == "fused_vt":
+            moga.moga_permute_vt(fwd.group_id, wl.M, Q, K, V, fwd.Qp, fwd.Kp, fwd.Vt, fwd.perm, fwd.cu_seqlens,
+                                 fwd.max_seqlen, fwd.ws_perm)
         else:
             moga.moga_permute(fwd.group_id, wl.M, Q, K, V, fwd.Qp, fwd.Kp, fwd.Vp, fwd.perm, fwd.cu_seqlens,
                               fwd.max_seqlen, fwd.ws_perm)
@@ -218,6 +223,9 @@ def main():
         elif args.path == "fused_epilogue":
             moga.moga_group_attention_unpermute(fwd.Qp, fwd.Kp, fwd.Vp, fwd.cu_seqlens, fwd.perm, fwd.gate, 0.0,
                                                 0.0, fwd.O, fwd.ws_attn)
+        elif args.path == "fused_vt":
+            moga.moga_group_attention_unpermute_vt(fwd.Qp, fwd.Kp, fwd.Vt, fwd.cu_seqlens, fwd.perm, fwd.gate, 0.0,
+                                                   0.0, fwd.O, fwd.ws_attn)
         else:
             moga.moga_group_attention(fwd.Qp, fwd.Kp, fwd.Vp, fwd.cu_seqlens, 0.0, fwd.Op, fwd.ws_attn)
             moga.moga_unpermute(fwd.Op, fwd.perm, fwd.gate, 0.0, fwd.O)

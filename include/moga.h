@@ -132,6 +132,38 @@ int moga_group_attention_unpermute(const void* Qp, const void* Kp, const void* V
                                    float beta, void* O, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moga_permute_vt -- moga_permute with V written transposed per head, the
+ *   layout moga_group_attention_unpermute_vt reads (Algorithm 1 step 2).
+ *   Qp, Kp   bf16 [N, H, D] (outputs) as in moga_permute
+ *   Vt       bf16 [H, D, ldv] (output), ldv = N rounded up to a multiple of
+ *            64, plus 64: Vt[h][d][j] = V[perm[j]][h][d] for j < N and 0 for
+ *            N <= j < ldv; 16-byte aligned.  The padding lets every 64-key
+ *            tile of the attention read whole rows.
+ *   Other arguments, workspace and errors as in moga_permute; all row
+ *   pointers are required.  N <= 2^23 - 128 (MOGA_ERR_UNSUPPORTED beyond):
+ *   the attention kernel addresses one head's V^T rows with 32-bit offsets.
+ */
+int moga_permute_vt(const int32_t* group_id, const void* Q, const void* K, const void* V,
+                    int64_t N, int32_t H, int32_t D, int32_t M,
+                    void* Qp, void* Kp, void* Vt, int32_t* perm, int32_t* cu_seqlens,
+                    int32_t* max_seqlen, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moga_group_attention_unpermute_vt -- moga_group_attention_unpermute with
+ *   V given transposed (Vt [H, D, ldv] as written by moga_permute_vt,
+ *   padding included; MoGA output equation, Algorithm 1 steps 3 and 4).  Same
+ *   result, up to float32 summation order, as the row layout: in LDS a
+ *   channel's 8 consecutive keys are one 16-byte read, where rows need two
+ *   transposing reads per MFMA operand.  Qp, Kp bf16 [N, H, D]; other
+ *   arguments, workspace and errors as in moga_group_attention_unpermute;
+ *   N <= 2^23 - 128.
+ */
+int moga_group_attention_unpermute_vt(const void* Qp, const void* Kp, const void* Vt,
+                                      const int32_t* cu_seqlens, const int32_t* perm, const float* gate,
+                                      int64_t N, int32_t H, int32_t D, int32_t M, float softmax_scale,
+                                      float beta, void* O, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * moga_group_attention_fused -- the gated group attention read in place
  *   (gather on load; MoGA output equation, Algorithm 1 steps 2 to 4 after the
  *   sort): Q, K, V are the ORIGINAL-order tensors bf16 [N, H, D], and

@@ -10,6 +10,8 @@ from ._lib import (MOGA_OP_BALANCE_STATS, MOGA_OP_GROUP_ATTENTION, MOGA_OP_PERMU
 from .binding import (MogaForward, MogaTraining, moga_balance_stats, moga_group_attention,  # noqa: F401
                       moga_group_attention_backward, moga_group_attention_train, moga_route_backward,
                       moga_unpermute_backward,
-                      moga_group_attention_fused, moga_group_attention_unpermute, moga_permute, moga_route,
+                      moga_group_attention_fused, moga_group_attention_unpermute,
+                      moga_group_attention_unpermute_vt, moga_permute, moga_permute_vt, moga_route,
+                      moga_vt_row_length,
                       moga_stga_attention, moga_stga_shot_attention, moga_stga_shot_workspace_bytes, moga_unpermute,
                       moga_workspace_bytes)

@@ -73,6 +73,7 @@ struct MogaRows {
   static constexpr bool kIndirect = false;
   static constexpr bool kContiguous = true;  // key row i of a group is row0 + i
   static constexpr bool kTable = false;
+  static constexpr bool kVt = false;
   const int32_t* cu;
   const AttnSchedule* sched;
   int M, H;
@@ -97,6 +98,21 @@ struct MogaRows {
   __device__ __forceinline__ int64_t key(const Work& w, int i) const { return w.row0 + i; }
 };
 
+// Learned groups with V stored transposed per head: Vt [H][D][ldv], the keys
+// of one channel contiguous and zero-padded (moga_permute_vt writes it).  A V operand of the
+// P V product is then one 16-byte LDS read instead of two transposing reads.
+struct MogaVtRows {
+  static constexpr bool kIndirect = false;
+  static constexpr bool kContiguous = true;
+  static constexpr bool kTable = false;
+  static constexpr bool kVt = true;
+  MogaRows base;
+  int64_t ldv;  // tokens per V^T row (N plus zero padding)
+  __device__ __forceinline__ bool decode(int item, Work& w) const { return base.decode(item, w); }
+  __device__ __forceinline__ int64_t row(const Work& w, int i) const { return w.row0 + i; }
+  __device__ __forceinline__ int64_t key(const Work& w, int i) const { return w.row0 + i; }
+};
+
 // Learned groups read in place (gather on load): permuted row j of a group is
 // original token perm[j], so Q, K and V are the unpermuted tensors and no
 // gathered copies exist.  Key rows are fetched a tile ahead (kIndirect).
@@ -104,6 +120,7 @@ struct MogaPermRows {
   static constexpr bool kIndirect = true;
   static constexpr bool kContiguous = false;
   static constexpr bool kTable = false;
+  static constexpr bool kVt = false;
   MogaRows base;
   const int32_t* perm;
   __device__ __forceinline__ bool decode(int item, Work& w) const { return base.decode(item, w); }
@@ -116,6 +133,7 @@ struct StgaRows {
   static constexpr bool kIndirect = false;
   static constexpr bool kContiguous = false;
   static constexpr bool kTable = true;  // key rows tabulated in LDS once per item
+  static constexpr bool kVt = false;
   int Hs, Ws, win_t, tile_h, tile_w, nty, ntx, tiles_per_group, H, items;
   __device__ __forceinline__ bool decode(int item, Work& w) const {
     if (item >= items) return false;
@@ -162,6 +180,7 @@ struct ShotRows {
   static constexpr bool kIndirect = false;
   static constexpr bool kContiguous = false;
   static constexpr bool kTable = true;
+  static constexpr bool kVt = false;
   const ShotWindow* win;
   const int* nwin;
   int Hs, Ws, tile_h, tile_w, ntx, nspatial, tpg, H;
@@ -329,6 +348,33 @@ __device__ __forceinline__ void issue_tile_buf(i32x4v krs, i32x4v vrs, uint16_t*
   }
 }
 
+// Transposed-V tiles (MogaVtRows).  The K rows of each 16-key block sit in
+// LDS with key bits 2 and 3 swapped (physical row r holds key swap23(r)): the
+// score rows one lane half holds for a 16-key MFMA step are then 8
+// consecutive keys, which is exactly what one 16-byte read of a V^T row
+// supplies.  The V^T tile is D channel rows of the tile's 64 keys (128
+// bytes); chunk p of channel row r sits at chunk p ^ ((r >> 1) & 7), which
+// keeps any 16 consecutive rows conflict-free for the 16-byte reads.
+__device__ __forceinline__ int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+__device__ __forceinline__ int vtswz(int r) { return (r >> 1) & 7; }
+
+template <int D, int NW>
+__device__ __forceinline__ void issue_tile_vt(i32x4v krs, i32x4v vrs, uint16_t* Ks, uint16_t* Vs,
+                                              int64_t row_stride, int64_t ldv, int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int LOADS = kBN * CPR / (NW * kWave);  // the V^T tile (D rows x 8 chunks) has as many chunks
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) {
+    const int q = (wave * LOADS + j) * kWave + lane;
+    const int lds_off = (wave * LOADS + j) * kWave * 8;
+    const int r = q / CPR, p = q % CPR;  // K: physical row r, chunk p
+    raw_buffer_load_lds(krs, (lds_void*)(Ks + lds_off), 16,
+                        swap23(r) * (int)row_stride * 2 + ((p ^ kswz(r, CPR)) << 4), 0, 0, 0);
+    const int vr = q >> 3, vp = q & 7;  // V^T: channel row vr, chunk vp
+    raw_buffer_load_lds(vrs, (lds_void*)(Vs + lds_off), 16, vr * (int)ldv * 2 + ((vp ^ vtswz(vr)) << 4), 0, 0, 0);
+  }
+}
+
 // Gather-on-load variant of issue_tile: the token row of every chunk this
 // lane loads was fetched beforehand (fetch_keys) into kidx.
 template <int D, int NW>
@@ -433,12 +479,34 @@ __device__ __forceinline__ void pv_half(const uint16_t* Vs, const bf16x8 (&p)[QB
   }
 }
 
-template <bool kMask, int QB>
+// pv_half with V^T in LDS (MogaVtRows): the operand of channel block db and
+// 16-key step t is one 16-byte read of channel row 32*db + lane%32, keys
+// 32*kb + 16*t + 8*hh .. +7, matching P's slots under the swapped K rows.
+template <int D, int QB>
+__device__ __forceinline__ void pv_half_t(const uint16_t* Vs, const bf16x8 (&p)[QB][2], int kb, int lane,
+                                          f32x16 (&o)[QB][D / 32]) {
+  const int hh = lane >> 5;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int r = 32 * db + (lane & 31);
+      const int c = (4 * kb + 2 * t + hh) ^ vtswz(r);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vs + r * kBN + c * 8);
+#pragma unroll
+      for (int b = 0; b < QB; ++b) o[b][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[b][t], o[b][db], 0, 0, 0);
+    }
+  }
+}
+
+template <bool kMask, int QB, bool kPermK = false>
 __device__ __forceinline__ void mask_half(f32x16 (&s)[QB], int key0, int len, int hh) {
   if constexpr (kMask) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      if (key0 + 8 * (r >> 2) + 4 * hh + (r & 3) >= len) {
+      int m = 8 * (r >> 2) + 4 * hh + (r & 3);  // LDS row of reg r in the half
+      if constexpr (kPermK) m = swap23(m);      // its key
+      if (key0 + m >= len) {
 #pragma unroll
         for (int b = 0; b < QB; ++b) s[b][r] = -INFINITY;
       }
@@ -448,7 +516,7 @@ __device__ __forceinline__ void mask_half(f32x16 (&s)[QB], int key0, int len, in
 
 // One 64-key tile for the wave's query blocks, in 32-key halves:
 //   QK(h0) QK(h1) | softmax(h0) PV(h0) | softmax(h1) PV(h1)
-template <int D, int QB, bool kMask>
+template <int D, int QB, bool kMask, bool kVt>
 __device__ __forceinline__ void tile_step(const uint16_t* Ks, const uint16_t* Vs, int k0, int len,
                                           const bf16x8 (&qf)[QB][D / 16], f32x16 (&o)[QB][D / 32],
                                           RowState (&rs)[QB], float scale_log2, int lane) {
@@ -457,18 +525,24 @@ __device__ __forceinline__ void tile_step(const uint16_t* Ks, const uint16_t* Vs
   bf16x8 p[QB][2];
   qk_half<D, QB>(Ks, qf, 0, lane, s0);
   qk_half<D, QB>(Ks, qf, 1, lane, s1);
-  mask_half<kMask, QB>(s0, k0, len, hh);
+  mask_half<kMask, QB, kVt>(s0, k0, len, hh);
 #pragma unroll
   for (int b = 0; b < QB; ++b) softmax_half(s0[b], rs[b], scale_log2, p[b]);
-  pv_half<D, QB>(Vs, p, 0, lane, o);
-  mask_half<kMask, QB>(s1, k0 + 32, len, hh);
+  if constexpr (kVt)
+    pv_half_t<D, QB>(Vs, p, 0, lane, o);
+  else
+    pv_half<D, QB>(Vs, p, 0, lane, o);
+  mask_half<kMask, QB, kVt>(s1, k0 + 32, len, hh);
 #pragma unroll
   for (int b = 0; b < QB; ++b) softmax_half(s1[b], rs[b], scale_log2, p[b]);
-  pv_half<D, QB>(Vs, p, 1, lane, o);
+  if constexpr (kVt)
+    pv_half_t<D, QB>(Vs, p, 1, lane, o);
+  else
+    pv_half<D, QB>(Vs, p, 1, lane, o);
 }
 
 // Row maxima only (the first pass of the exact recomputation).
-template <int D, int QB, bool kMask>
+template <int D, int QB, bool kMask, bool kVt>
 __device__ __forceinline__ void tile_max(const uint16_t* Ks, int k0, int len, const bf16x8 (&qf)[QB][D / 16],
                                          float (&mx)[QB], int lane) {
   const int hh = lane >> 5;
@@ -476,7 +550,7 @@ __device__ __forceinline__ void tile_max(const uint16_t* Ks, int k0, int len, co
   for (int kb = 0; kb < 2; ++kb) {
     f32x16 s[QB];
     qk_half<D, QB>(Ks, qf, kb, lane, s);
-    mask_half<kMask, QB>(s, k0 + 32 * kb, len, hh);
+    mask_half<kMask, QB, kVt>(s, k0 + 32 * kb, len, hh);
 #pragma unroll
     for (int b = 0; b < QB; ++b)
 #pragma unroll
@@ -536,7 +610,15 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave) void attn_kernel(
   // Tile t's K/V loads; with gather on load, also fetch tile t+1's key rows.
   [[maybe_unused]] int32_t kidx[tile_loads<D, NW>()];
   auto issue = [&](uint16_t* Kd, uint16_t* Vd, int t) {
-    if constexpr (Rows::kContiguous) {
+    if constexpr (Rows::kVt) {
+      // V^T rows of this head: channel d is V + (head * D + d) * ldv.  The
+      // tile's 64 keys lie inside the row (its padding is zeros), so the
+      // descriptor covers whole tiles; keys past the group end are masked.
+      const int64_t k0 = w.row0 + (int64_t)t * kBN;
+      issue_tile_vt<D, NW>(row_range_rsrc(K + k0 * row_stride + hoff, w.len - t * kBN, row_stride * 2, D * 2),
+                           row_range_rsrc(V + (int64_t)w.head * D * rows.ldv + k0, D, rows.ldv * 2, kBN * 2),
+                           Kd, Vd, row_stride, rows.ldv, wave, lane);
+    } else if constexpr (Rows::kContiguous) {
       const int64_t first = (w.row0 + (int64_t)t * kBN) * row_stride + hoff;
       const int64_t n_rows = w.len - t * kBN;
       issue_tile_buf<D, NW>(row_range_rsrc(K + first, n_rows, row_stride * 2, D * 2),
@@ -598,9 +680,9 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave) void attn_kernel(
       constexpr bool kMask = decltype(mask)::value;
       if (!wave_live) return;  // keeps its barriers and loads, skips the math
       if constexpr (kMax)
-        tile_max<D, QB, kMask>(Ks, t * kBN, w.len, qf, mx, lane);
+        tile_max<D, QB, kMask, Rows::kVt>(Ks, t * kBN, w.len, qf, mx, lane);
       else
-        tile_step<D, QB, kMask>(Ks, Vs, t * kBN, w.len, qf, o, rs, scale_log2, lane);
+        tile_step<D, QB, kMask, Rows::kVt>(Ks, Vs, t * kBN, w.len, qf, o, rs, scale_log2, lane);
     };
     using F = std::false_type;
     using T = std::true_type;
@@ -635,7 +717,7 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave) void attn_kernel(
   if (wave_live) {
     f32x16 s[QB];
     qk_half<D, QB>(Ks0, qf, 0, lane, s);
-    if (w.len < 32) mask_half<true, QB>(s, 0, w.len, hh);
+    if (w.len < 32) mask_half<true, QB, Rows::kVt>(s, 0, w.len, hh);
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
       float mx = s[b][0];
@@ -871,6 +953,28 @@ extern "C" int moga_group_attention_unpermute(const void* Qp, const void* Kp, co
   const Epilogue epi{1.f, beta, perm, gate, nullptr, 0};
   if (D == 128) return launch_attn<128, MogaRows, kEpiGated>(Qp, Kp, Vp, O, (int64_t)H * D, scale, epi, rows, bound, st);
   return launch_attn<64, MogaRows, kEpiGated>(Qp, Kp, Vp, O, (int64_t)H * D, scale, epi, rows, bound, st);
+}
+
+extern "C" int moga_group_attention_unpermute_vt(const void* Qp, const void* Kp, const void* Vt,
+                                                 const int32_t* cu_seqlens, const int32_t* perm, const float* gate,
+                                                 int64_t N, int32_t H, int32_t D, int32_t M, float softmax_scale,
+                                                 float beta, void* O, void* ws, size_t ws_bytes, void* stream) {
+  using namespace moga;
+  if (!Qp || !Kp || !Vt || !cu_seqlens || !perm || !gate || !O) return MOGA_ERR_NULL;
+  if (N < 1 || N >= (int64_t(1) << 31) || M < 1 || H < 1 || D < 1) return MOGA_ERR_SHAPE;
+  if (M > kMaxGroups || !valid_head_dims(H, D) || N > kVtMaxTokens) return MOGA_ERR_UNSUPPORTED;
+  const size_t need = moga_workspace_bytes(MOGA_OP_GROUP_ATTENTION, N, M, H, D);
+  if (!ws || ws_bytes < need) return MOGA_ERR_WORKSPACE;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
+  hipStream_t st = as_stream(stream);
+  auto* sched = static_cast<AttnSchedule*>(ws);
+  schedule_kernel<<<1, kWave, 0, st>>>(cu_seqlens, M, H, sched);
+  MOGA_LAUNCH_CHECK();
+  MogaVtRows rows{MogaRows{cu_seqlens, sched, M, H}, vt_row_length(N)};
+  const int64_t bound = (ceil_div(N, kBM) + M) * H;
+  const Epilogue epi{1.f, beta, perm, gate, nullptr, 0};
+  if (D == 128) return launch_attn<128, MogaVtRows, kEpiGated>(Qp, Kp, Vt, O, (int64_t)H * D, scale, epi, rows, bound, st);
+  return launch_attn<64, MogaVtRows, kEpiGated>(Qp, Kp, Vt, O, (int64_t)H * D, scale, epi, rows, bound, st);
 }
 
 extern "C" size_t moga_stga_shot_workspace_bytes(int32_t T, int32_t n_shots, int32_t win_t) {

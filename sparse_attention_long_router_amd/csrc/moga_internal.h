@@ -64,6 +64,14 @@ struct AttnSchedule {
   int32_t prefix[kMaxGroups + 1];
 };
 
+// Transposed-V layout Vt [H][D][ldv]: every channel row holds the N permuted
+// tokens and zero padding up to ldv = N rounded up to 64, plus 64, so a
+// 64-key tile starting at any key < N lies inside its row.  The attention
+// kernel addresses one head's V^T rows with 32-bit offsets, (D-1)*ldv*2 + 128
+// bytes, which bounds N.
+inline int64_t vt_row_length(int64_t N) { return (N + 63) / 64 * 64 + 64; }
+constexpr int64_t kVtMaxTokens = (int64_t(1) << 23) - 128;
+
 inline bool valid_head_dims(int32_t H, int32_t D) {
   return H >= 1 && (D == 64 || D == 128) && (int64_t)H * D <= 8192;
 }

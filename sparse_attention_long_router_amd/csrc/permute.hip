@@ -131,6 +131,7 @@ constexpr int kGatherBatch = 3;  // 64-lane chunk steps loaded before any store
 // wave copies one row of each tensor; all loads of a batch (three 1 KB
 // contiguous pieces per tensor, the whole row at H*D = 1536) are in flight
 // before the first store, which measured 4% faster than interleaving them.
+template <bool kWithV>
 __global__ __launch_bounds__(kGatherWaves * kWave) void gather_kernel(
     const int32_t* __restrict__ perm, int64_t N, int chunks, const u32x4* __restrict__ Q,
     const u32x4* __restrict__ K, const u32x4* __restrict__ V, u32x4* __restrict__ Qp, u32x4* __restrict__ Kp,
@@ -147,7 +148,7 @@ __global__ __launch_bounds__(kGatherWaves * kWave) void gather_kernel(
       if (c < chunks) {
         a[u] = __builtin_nontemporal_load(Q + src + c);
         b[u] = __builtin_nontemporal_load(K + src + c);
-        d[u] = __builtin_nontemporal_load(V + src + c);
+        if constexpr (kWithV) d[u] = __builtin_nontemporal_load(V + src + c);
       }
     }
 #pragma unroll
@@ -156,9 +157,52 @@ __global__ __launch_bounds__(kGatherWaves * kWave) void gather_kernel(
       if (c < chunks) {
         __builtin_nontemporal_store(a[u], Qp + dst + c);
         __builtin_nontemporal_store(b[u], Kp + dst + c);
-        __builtin_nontemporal_store(d[u], Vp + dst + c);
+        if constexpr (kWithV) __builtin_nontemporal_store(d[u], Vp + dst + c);
       }
     }
+  }
+}
+
+// Vt[h][d][j] = V[perm[j]][h][d] for j < N and 0 for N <= j < ldv: V in
+// permuted order, transposed per head (one zero-padded row per channel).  A
+// workgroup takes 64 consecutive permuted tokens of one head: it reads their
+// D-channel slices (D*2 contiguous bytes each) into LDS and writes D rows of
+// 64 tokens (128 contiguous bytes, eight lanes) back out.  The LDS row pitch
+// of D + 2 elements (65 dwords at D = 128) moves each row one bank on, so the
+// column reads of the transposition and the row writes are both free of bank
+// conflicts.
+constexpr int kVtTile = 64;
+template <int D>
+__global__ __launch_bounds__(256) void gather_vt_kernel(const int32_t* __restrict__ perm, int64_t N, int64_t ldv,
+                                                        int H, const uint16_t* __restrict__ V,
+                                                        uint16_t* __restrict__ Vt) {
+  constexpr int kPitch = D + 2;  // elements
+  constexpr int CPT = D / 8;     // 16-byte chunks per token slice
+  __shared__ __attribute__((aligned(16))) uint32_t tile[kVtTile * kPitch / 2];
+  const int h = blockIdx.y;
+  const int64_t j0 = (int64_t)blockIdx.x * kVtTile;  // ldv is a multiple of 64: the tile lies inside the row
+  for (int c = threadIdx.x; c < kVtTile * CPT; c += 256) {
+    const int tok = c / CPT, ch = c % CPT;
+    const int64_t j = j0 + tok;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (j < N) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(V + ((int64_t)perm[j] * H + h) * D) + ch);
+    uint32_t* row = tile + tok * (kPitch / 2) + ch * 4;
+    row[0] = v[0];
+    row[1] = v[1];
+    row[2] = v[2];
+    row[3] = v[3];
+  }
+  __syncthreads();
+  const uint16_t* t16 = reinterpret_cast<const uint16_t*>(tile);
+  // channel row d, tokens 8u .. 8u+7
+  for (int c = threadIdx.x; c < D * (kVtTile / 8); c += 256) {
+    const int d = c >> 3, u = c & 7;
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = (uint32_t)t16[(8 * u + 2 * i) * kPitch + d] | ((uint32_t)t16[(8 * u + 2 * i + 1) * kPitch + d] << 16);
+    __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]},
+                                reinterpret_cast<u32x4*>(Vt + ((int64_t)h * D + d) * ldv + j0 + 8 * u));
   }
 }
 
@@ -192,10 +236,39 @@ extern "C" int moga_permute(const int32_t* group_id, const void* Q, const void* 
   if (all_rows) {
     const int chunks = H * D / 8;
     const int64_t blocks = ceil_div(N, kGatherWaves);
-    gather_kernel<<<dim3((unsigned)blocks), kGatherWaves * kWave, 0, st>>>(
+    gather_kernel<true><<<dim3((unsigned)blocks), kGatherWaves * kWave, 0, st>>>(
         perm, N, chunks, static_cast<const u32x4*>(Q), static_cast<const u32x4*>(K), static_cast<const u32x4*>(V),
         static_cast<u32x4*>(Qp), static_cast<u32x4*>(Kp), static_cast<u32x4*>(Vp));
     MOGA_LAUNCH_CHECK();
   }
+  return MOGA_OK;
+}
+
+extern "C" int moga_permute_vt(const int32_t* group_id, const void* Q, const void* K, const void* V, int64_t N,
+                               int32_t H, int32_t D, int32_t M, void* Qp, void* Kp, void* Vt, int32_t* perm,
+                               int32_t* cu_seqlens, int32_t* max_seqlen, void* ws, size_t ws_bytes, void* stream) {
+  using namespace moga;
+  if (!group_id || !perm || !cu_seqlens || !max_seqlen || !Q || !K || !V || !Qp || !Kp || !Vt) return MOGA_ERR_NULL;
+  if (N < 1 || N >= (int64_t(1) << 31) || M < 1 || H < 1 || D < 1) return MOGA_ERR_SHAPE;
+  if (M > kMaxGroups || !valid_head_dims(H, D) || N > kVtMaxTokens) return MOGA_ERR_UNSUPPORTED;
+  // the sort, as moga_permute without row copies
+  const int rc = moga_permute(group_id, nullptr, nullptr, nullptr, N, H, D, M, nullptr, nullptr, nullptr, perm,
+                              cu_seqlens, max_seqlen, ws, ws_bytes, stream);
+  if (rc != MOGA_OK) return rc;
+  hipStream_t st = as_stream(stream);
+  const int chunks = H * D / 8;
+  gather_kernel<false><<<dim3((unsigned)ceil_div(N, kGatherWaves)), kGatherWaves * kWave, 0, st>>>(
+      perm, N, chunks, static_cast<const u32x4*>(Q), static_cast<const u32x4*>(K), nullptr,
+      static_cast<u32x4*>(Qp), static_cast<u32x4*>(Kp), nullptr);
+  MOGA_LAUNCH_CHECK();
+  const int64_t ldv = vt_row_length(N);
+  const dim3 grid((unsigned)(ldv / kVtTile), (unsigned)H);
+  if (D == 128)
+    gather_vt_kernel<128><<<grid, 256, 0, st>>>(perm, N, ldv, H, static_cast<const uint16_t*>(V),
+                                               static_cast<uint16_t*>(Vt));
+  else
+    gather_vt_kernel<64><<<grid, 256, 0, st>>>(perm, N, ldv, H, static_cast<const uint16_t*>(V),
+                                              static_cast<uint16_t*>(Vt));
+  MOGA_LAUNCH_CHECK();
   return MOGA_OK;
 }

@@ -70,6 +70,17 @@ def _full_check(moga, inp, bias=None, label=""):
     torch.cuda.synchronize()
     assert_output_close(_np(Og), ref["O"], "O (gather on load)")
     assert torch.equal(Og, Of)   # same rows, same key order, same arithmetic
+    # transposed-V layout: the same gathered rows, V as [H, D, N]
+    pv = moga.moga_permute_vt(gid, M, Q, K, V)
+    assert torch.equal(pv["perm"], p["perm"]) and torch.equal(pv["cu_seqlens"], p["cu_seqlens"])
+    assert torch.equal(pv["Qp"], p["Qp"]) and torch.equal(pv["Kp"], p["Kp"])
+    N = X.shape[0]
+    assert pv["Vt"].shape[2] == moga.moga_vt_row_length(N)
+    assert torch.equal(pv["Vt"][:, :, :N], p["Vp"].permute(1, 2, 0))
+    assert not pv["Vt"][:, :, N:].any()          # zero padding
+    Ot = moga.moga_group_attention_unpermute_vt(pv["Qp"], pv["Kp"], pv["Vt"], pv["cu_seqlens"], pv["perm"], gate)
+    torch.cuda.synchronize()
+    assert_output_close(_np(Ot), ref["O"], "O (transposed V)")
     print(f"[parity] {label} Op {e_attn} O {e_out}", flush=True)
     return gid, gate, p, Op, O, ref
 
@@ -222,9 +233,10 @@ def test_stga_shot(moga, T, Hs, Ws, shots, win_t, th, tw, aug, H, D, alpha, beta
 # Full workload sizes, in the launch configuration the benchmark times
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name,path", [("wan13b_21f", "fused_epilogue"), ("clip30s_122f", "fused_epilogue"),
-                                       ("clip30s_122f", "gather_on_load"), ("clip30s_122f", "separate"),
-                                       ("wan14b_122f", "fused_epilogue"), ("minute_372f", "fused_epilogue"),
+@pytest.mark.parametrize("name,path", [("wan13b_21f", "fused_vt"), ("clip30s_122f", "fused_vt"),
+                                       ("clip30s_122f", "fused_epilogue"), ("clip30s_122f", "gather_on_load"),
+                                       ("clip30s_122f", "separate"), ("wan14b_122f", "fused_vt"),
+                                       ("minute_372f", "fused_vt"), ("minute_372f", "fused_epilogue"),
                                        ("minute_372f", "gather_on_load")])
 def test_full_size_sampled(moga, name, path):
     wl = get_workload(name)
