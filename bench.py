@@ -252,9 +252,12 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
 
     stages = ["route", "permute", "group_attention", "stga"]
-    breakdown = {s: sum(e[k].elapsed_time(e[k + 1]) for e in evs) / args.steps for k, s in enumerate(stages)}
+    per_step = {s: sorted(e[k].elapsed_time(e[k + 1]) for e in evs) for k, s in enumerate(stages)}
     if wl.stga is None:
-        breakdown.pop("stga")
+        per_step.pop("stga")
+    breakdown = {s: sum(v) / len(v) for s, v in per_step.items()}
+    stage_stats = {s: {"median": round(v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2]), 4),
+                       "min": round(v[0], 4)} for s, v in per_step.items()}
 
     counts = (fwd.cu_seqlens[1:] - fwd.cu_seqlens[:-1]).cpu().tolist()
     flops_moga = attn_flops(counts, wl.H, wl.D)
@@ -294,6 +297,7 @@ def main():
         "tokens_per_s": round(wl.N / (ms_per_step * 1e-3), 1),
         "mfma_frac_step": round(value / PEAK_BF16_TFLOPS, 4),
         "breakdown_ms": {k: round(v, 4) for k, v in breakdown.items()},
+        "stage_ms": stage_stats,
         "roofline": roofline,
         "cpu_baseline": None,
     }
