@@ -38,7 +38,7 @@ constexpr int kDqBM = 256;     // queries per dq work item (8 waves x 32)
 constexpr int kDqWaves = 8;
 constexpr int kDkvBN = 128;    // keys per dkdv work item (4 waves x 32)
 constexpr int kDkvWaves = 4;
-constexpr int kRun = 8;        // consecutive items per XCD
+constexpr int kRun = 32;       // consecutive items per XCD, one per CU: about half the HBM reads of 8
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
