@@ -16,6 +16,10 @@
 //                   are ordered through LDS counts -> perm[base + rank] = n
 //   gather_kernel   Qp/Kp/Vp[j] = Q/K/V[perm[j]], whole H*D rows, 16-byte
 //                   lanes, one wave per row copy (HBM-bound stream)
+// moga_permute_vt runs the same sort, gathers only Q and K as rows and
+// writes V transposed per head (gather_vt_kernel): Vt[h][d][j], the layout
+// whose 64-key tiles the attention reads with one 16-byte LDS read per MFMA
+// operand.
 #include "moga_internal.h"
 
 namespace moga {
