@@ -20,9 +20,12 @@
 // Rows past a group's end are read as zeros through the buffer range check:
 // a zero query row has a zero upstream gradient and a zero key row a zero
 // operand, so they add nothing to the rows that are stored, and the exact
-// P = exp(s - lse) needs no normaliser.  The dq kernel still gives the zero
-// key rows of a group's last tile no weight, so that a very negative
-// log-sum-exp cannot turn them into inf * 0.
+// P = exp(s - lse) needs no normaliser.  The dq kernel clamps the exponent
+// at 2^0.5 (a valid key's weight is at most 1), so that a very negative
+// log-sum-exp cannot turn the zero key rows of a group's last tile into
+// inf * 0.
+#include <type_traits>
+
 #include "moga_internal.h"
 
 typedef int32_t i32x4v __attribute__((ext_vector_type(4)));
@@ -84,8 +87,10 @@ __device__ __forceinline__ void load_tile(i32x4v rs, uint16_t* T, int64_t row_st
 
 // A from 32 LDS rows (rbase..rbase+31), B from registers: C[m = row][n = lane % 32].
 // Reg r of the result is row 8*(r/4) + 4*hh + r%4 of the block.
+// c0 is the accumulator's starting value (zeros, or a per-row offset).
 template <int D, int kSwz>
-__device__ __forceinline__ f32x16 rows_mma(const uint16_t* T, int rbase, const bf16x8 (&b)[D / 16], int lane) {
+__device__ __forceinline__ f32x16 rows_mma(const uint16_t* T, int rbase, const bf16x8 (&b)[D / 16], int lane,
+                                           f32x16 c0 = f32x16{}) {
   constexpr int CPR = D / 8;
   const int hh = lane >> 5, row = rbase + (lane & 31);
   bf16x8 a[D / 16];
@@ -93,7 +98,7 @@ __device__ __forceinline__ f32x16 rows_mma(const uint16_t* T, int rbase, const b
   for (int st = 0; st < D / 16; ++st)
     a[st] = *reinterpret_cast<const bf16x8*>(T + row * D + ((2 * st + hh) ^ swz<kSwz>(row, CPR)) * 8);
   __builtin_amdgcn_sched_barrier(0);
-  f32x16 c = {};
+  f32x16 c = c0;
 #pragma unroll
   for (int st = 0; st < D / 16; ++st) c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[st], b[st], c, 0, 0, 0);
   return c;
@@ -216,7 +221,8 @@ __global__ __launch_bounds__(kDkvWaves * kWave) void dkdv_kernel(
 
   Item w;
   if (!decode(sched, cu, M, kDkvBN, xcd_remap(blockIdx.x, kRun), w)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar descriptors, no waterfall
   const int64_t hoff = (int64_t)w.head * D;
   const int ntiles = (w.len + kTile - 1) / kTile;
   const float c2 = scale * 1.4426950408889634f;  // scores to log2 units
@@ -257,25 +263,40 @@ __global__ __launch_bounds__(kDkvWaves * kWave) void dkdv_kernel(
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     __builtin_amdgcn_s_waitcnt(0);
+    if (wave < kTile / kWave) {
+      // This wave's lse and delta entries of the tile have landed: turn them
+      // into the forms the loop consumes, lse in log2 units and -delta (the
+      // starting value of the dP accumulator, so that it yields dP - delta).
+      const int o = wave * kWave + lane;
+      Ls[buf][o] *= 1.4426950408889634f;
+      Ds[buf][o] = -Ds[buf][o];
+    }
     __syncthreads();
     if (t + 1 < ntiles) issue(buf ^ 1, t + 1);
     const uint16_t* Qt = Qs[buf];
     const uint16_t* At = As[buf];
 #pragma unroll
     for (int qb = 0; qb < kTile / 32; ++qb) {
-      const f32x16 s = rows_mma<D, kBoth>(Qt, qb * 32, kf, lane);   // S[query][key]
-      const f32x16 dp = rows_mma<D, kBoth>(At, qb * 32, vf, lane);  // dP[query][key]
+      // reg r of a C-layout block is row qb*32 + 8*(r/4) + 4*hh + r%4
+      f32x16 nd;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Ds[buf][qb * 32 + 8 * g + 4 * hh]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) nd[4 * g + i] = d4[i];
+      }
+      const f32x16 s = rows_mma<D, kBoth>(Qt, qb * 32, kf, lane);       // S[query][key]
+      const f32x16 dp = rows_mma<D, kBoth>(At, qb * 32, vf, lane, nd);  // dP[query][key] - delta[query]
       bf16x8 pb[2], sb[2];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {  // rows qb*32 + 8g + 4hh + 0..3
+      for (int g = 0; g < 4; ++g) {
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Ls[buf][qb * 32 + 8 * g + 4 * hh]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Ds[buf][qb * 32 + 8 * g + 4 * hh]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * g + i;
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l4[i] * 1.4426950408889634f));
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l4[i]));
           pb[r >> 3][r & 7] = (__bf16)p;
-          sb[r >> 3][r & 7] = (__bf16)(p * (dp[r] - d4[i]));
+          sb[r >> 3][r & 7] = (__bf16)(p * dp[r]);
         }
       }
       tr_mma<D, kBoth>(At, qb * 32, pb, lane, dv);  // dV^T += dA^T P
@@ -307,7 +328,8 @@ __global__ __launch_bounds__(kDqWaves * kWave) void dq_kernel(
 
   Item w;
   if (!decode(sched, cu, M, kDqBM, xcd_remap(blockIdx.x, kRun), w)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t hoff = (int64_t)w.head * D;
   const int ntiles = (w.len + kTile - 1) / kTile;
   const float c2 = scale * 1.4426950408889634f;
@@ -352,12 +374,14 @@ __global__ __launch_bounds__(kDqWaves * kWave) void dq_kernel(
         dp = rows_mma<D, kRowsOnly>(Vs[buf], kb * 32, af, lane);
       }
       bf16x8 sb[2];
-      // keys past the group end (zero rows, last tile only) get no weight
-      const int kend = t + 1 < ntiles ? kTile : w.len - t * kTile;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int kk = kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-        const float p = kk < kend ? __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l2)) : 0.f;
+        // A key of the group has s * c2 <= l2 (the log-sum-exp bounds every
+        // term), so the exponent is at most a rounding error above 0 and the
+        // clamp never binds.  The zero key rows past the group end have s = 0,
+        // where a very negative log-sum-exp would overflow p and turn their
+        // zero product into inf * 0; clamped, p stays finite and they add 0.
+        const float p = __builtin_amdgcn_exp2f(fminf(fmaf(s[r], c2, -l2), 0.5f));
         sb[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dl));
       }
       tr_mma<D, kBoth>(Ks[buf], kb * 32, sb, lane, dq);  // dQ^T += K^T dS^T
