@@ -5,10 +5,12 @@
 A step is one pass of the whole path over one synthetic batch already resident
 in HBM: route -> permute -> gated group attention (-> STGA sum for workloads
 that have it).  --path picks how attention meets the permutation (default
-fused_vt: sort + Q/K gather + V gathered transposed per head, attention with
-the gated unpermute in its epilogue; fused_epilogue: the same with V in row
-layout; gather_on_load: sort only, attention reads Q/K/V rows through perm and
-writes the gated output in place; separate: gather, attention, unpermute).
+fused_vtq: sort + K gather + V gathered transposed per head, attention reading
+each query row through perm, with the gated unpermute in its epilogue;
+fused_vt: the same with a gathered Q copy; fused_epilogue: as fused_vt with V
+in row layout; gather_on_load: sort only, attention reads Q/K/V rows
+through perm and writes the gated output in place; separate: gather,
+attention, unpermute).
 Prints ONE JSON line.
 
 value = effective TFLOP/s of the whole step, counting only within-group
@@ -44,8 +46,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--path", default="fused_vt",
-                    choices=["fused_vt", "fused_epilogue", "gather_on_load", "separate"])
+    ap.add_argument("--path", default="fused_vtq",
+                    choices=["fused_vtq", "fused_vt", "fused_epilogue", "gather_on_load", "separate"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass timing")
     ap.add_argument("--cpu-rows", type=int, default=2000, help="sampled query rows per group for the oracle")
@@ -196,6 +198,7 @@ def main():
     attn_kernel = {"gather_on_load": "attn_kernel (moga_group_attention_fused)",
                    "fused_epilogue": "attn_kernel (moga_group_attention_unpermute)",
                    "fused_vt": "attn_kernel (moga_group_attention_unpermute_vt)",
+                   "fused_vtq": "attn_kernel (moga_group_attention_unpermute_vtq)",
                    "separate": "attn_kernel (moga_group_attention) + unpermute_kernel"}[args.path]
 
     def step(ev=None):
@@ -212,6 +215,9 @@ def main():
         elif args.path == "fused_vt":
             moga.moga_permute_vt(fwd.group_id, wl.M, Q, K, V, fwd.Qp, fwd.Kp, fwd.Vt, fwd.perm, fwd.cu_seqlens,
                                  fwd.max_seqlen, fwd.ws_perm)
+        elif args.path == "fused_vtq":
+            moga.moga_permute_vt(fwd.group_id, wl.M, None, K, V, None, fwd.Kp, fwd.Vt, fwd.perm, fwd.cu_seqlens,
+                                 fwd.max_seqlen, fwd.ws_perm)
         else:
             moga.moga_permute(fwd.group_id, wl.M, Q, K, V, fwd.Qp, fwd.Kp, fwd.Vp, fwd.perm, fwd.cu_seqlens,
                               fwd.max_seqlen, fwd.ws_perm)
@@ -226,6 +232,9 @@ def main():
         elif args.path == "fused_vt":
             moga.moga_group_attention_unpermute_vt(fwd.Qp, fwd.Kp, fwd.Vt, fwd.cu_seqlens, fwd.perm, fwd.gate, 0.0,
                                                    0.0, fwd.O, fwd.ws_attn)
+        elif args.path == "fused_vtq":
+            moga.moga_group_attention_unpermute_vtq(Q, fwd.Kp, fwd.Vt, fwd.cu_seqlens, fwd.perm, fwd.gate, 0.0,
+                                                    0.0, fwd.O, fwd.ws_attn)
         else:
             moga.moga_group_attention(fwd.Qp, fwd.Kp, fwd.Vp, fwd.cu_seqlens, 0.0, fwd.Op, fwd.ws_attn)
             moga.moga_unpermute(fwd.Op, fwd.perm, fwd.gate, 0.0, fwd.O)
@@ -305,7 +314,10 @@ def main():
         del fwd  # free the forward buffers before the training ones
         out["backward"] = backward_timing(moga, wl, X, Wr, Q, K, V, flops_moga, steps=max(2, args.steps // 4))
     hbm = {"route": wl.N * (2 * wl.d_model + 8) + 2 * wl.M * wl.d_model}  # algorithmic bytes per launch
-    if args.path != "gather_on_load":  # sort + gather; the sort alone is latency-bound (reported in ms only)
+    # sort + gather; the sort alone is latency-bound (reported in ms only)
+    if args.path == "fused_vtq":  # K and V gathered, Q read through perm by the attention
+        hbm["permute"] = wl.N * (8 * wl.H * wl.D + 16)
+    elif args.path != "gather_on_load":
         hbm["permute"] = wl.N * (12 * wl.H * wl.D + 16)
     out["hbm_gbs"] = {k: round(b / (breakdown[k] * 1e-3) / 1e9, 1) for k, b in hbm.items()}
     out["hbm_frac"] = {k: round(v / PEAK_HBM_GBS, 4) for k, v in out["hbm_gbs"].items()}

@@ -139,9 +139,12 @@ int moga_group_attention_unpermute(const void* Qp, const void* Kp, const void* V
  *            64, plus 64: Vt[h][d][j] = V[perm[j]][h][d] for j < N and 0 for
  *            N <= j < ldv; 16-byte aligned.  The padding lets every 64-key
  *            tile of the attention read whole rows.
- *   Other arguments, workspace and errors as in moga_permute; all row
- *   pointers are required.  N <= 2^23 - 128 (MOGA_ERR_UNSUPPORTED beyond):
- *   the attention kernel addresses one head's V^T rows with 32-bit offsets.
+ *   Other arguments, workspace and errors as in moga_permute.  K, V, Kp and
+ *   Vt are required; Q and Qp are either both given (Q is gathered) or both
+ *   NULL (only K and V are gathered, for moga_group_attention_unpermute_vtq;
+ *   one of the two alone is MOGA_ERR_NULL).  N <= 2^23 - 128
+ *   (MOGA_ERR_UNSUPPORTED beyond): the attention kernel addresses one head's
+ *   V^T rows with 32-bit offsets.
  */
 int moga_permute_vt(const int32_t* group_id, const void* Q, const void* K, const void* V,
                     int64_t N, int32_t H, int32_t D, int32_t M,
@@ -162,6 +165,24 @@ int moga_group_attention_unpermute_vt(const void* Qp, const void* Kp, const void
                                       const int32_t* cu_seqlens, const int32_t* perm, const float* gate,
                                       int64_t N, int32_t H, int32_t D, int32_t M, float softmax_scale,
                                       float beta, void* O, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moga_group_attention_unpermute_vtq -- moga_group_attention_unpermute_vt
+ *   with the queries read in original token order (MoGA output equation,
+ *   Algorithm 1 steps 3 and 4): Q is the UNPERMUTED bf16 [N, H, D] tensor and
+ *   query j of the permuted order is token perm[j], so moga_permute_vt may
+ *   skip the Q gather (Q = Qp = NULL there).  Kp bf16 [N, H, D] and
+ *   Vt [H, D, ldv] as written by moga_permute_vt.  Each query row is read
+ *   once per work item, so reading it through perm costs one index load,
+ *   where a gathered copy costs a read and a write of every row.
+ *   O[n] = beta * O[n] + gate[n] * Attn(n); same result, bit for bit, as
+ *   moga_group_attention_unpermute_vt on the gathered Qp.  Other arguments,
+ *   workspace and errors as there; O must not alias Q, Kp or Vt.
+ */
+int moga_group_attention_unpermute_vtq(const void* Q, const void* Kp, const void* Vt,
+                                       const int32_t* cu_seqlens, const int32_t* perm, const float* gate,
+                                       int64_t N, int32_t H, int32_t D, int32_t M, float softmax_scale,
+                                       float beta, void* O, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moga_group_attention_fused -- the gated group attention read in place

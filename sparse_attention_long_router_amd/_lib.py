@@ -38,6 +38,8 @@ SIGNATURES = {
                                    _vp, _sz, _vp]),
     "moga_group_attention_unpermute_vt": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _f32,
                                                       _f32, _vp, _vp, _sz, _vp]),
+    "moga_group_attention_unpermute_vtq": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _f32,
+                                                       _f32, _vp, _vp, _sz, _vp]),
     "moga_group_attention_fused": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _f32, _f32,
                                               _vp, _vp, _sz, _vp]),
     "moga_unpermute": (_c.c_int, [_vp, _vp, _vp, _i64, _i32, _i32, _f32, _vp, _vp]),

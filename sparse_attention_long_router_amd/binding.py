@@ -146,22 +146,27 @@ def moga_permute_vt(group_id, M, Q, K, V, Qp=None, Kp=None, Vt=None, perm=None, 
                     max_seqlen=None, ws=None):
     """moga_permute with V written transposed per head: Vt bf16 [H, D, ldv]
     (ldv = moga_vt_row_length(N)), Vt[h, d, j] = V[perm[j], h, d] for j < N,
-    zeros after.  Returns a dict (Qp, Kp, Vt, perm, cu_seqlens, max_seqlen)."""
+    zeros after.  Q = None skips the Q gather (for
+    moga_group_attention_unpermute_vtq, which reads Q through perm).  Returns
+    a dict (Qp, Kp, Vt, perm, cu_seqlens, max_seqlen); Qp is None without Q."""
     _need(group_id, "group_id", torch.int32, 1)
     N = group_id.shape[0]
     dev = group_id.device
-    _need(Q, "Q", BF16, 3)
-    H, D = Q.shape[1], Q.shape[2]
-    for name, t in (("K", K), ("V", V)):
-        _need(t, name, BF16, 3, Q.shape)
-    if Q.shape[0] != N:
-        raise ValueError("Q rows must match group_id")
-    Qp = torch.empty_like(Q) if Qp is None else Qp
+    _need(K, "K", BF16, 3)
+    H, D = K.shape[1], K.shape[2]
+    _need(V, "V", BF16, 3, K.shape)
+    if K.shape[0] != N:
+        raise ValueError("K rows must match group_id")
+    if Q is not None:
+        _need(Q, "Q", BF16, 3, K.shape)
+        Qp = torch.empty_like(Q) if Qp is None else Qp
+        _need(Qp, "Qp", BF16, 3, K.shape)
+    elif Qp is not None:
+        raise ValueError("Qp given without Q")
     Kp = torch.empty_like(K) if Kp is None else Kp
     ldv = moga_vt_row_length(N)
     Vt = torch.empty((H, D, ldv), dtype=BF16, device=dev) if Vt is None else Vt
-    for name, t in (("Qp", Qp), ("Kp", Kp)):
-        _need(t, name, BF16, 3, Q.shape)
+    _need(Kp, "Kp", BF16, 3, K.shape)
     _need(Vt, "Vt", BF16, 3, (H, D, ldv))
     perm = torch.empty(N, dtype=torch.int32, device=dev) if perm is None else perm
     cu_seqlens = torch.empty(M + 1, dtype=torch.int32, device=dev) if cu_seqlens is None else cu_seqlens
@@ -198,6 +203,31 @@ def moga_group_attention_unpermute_vt(Qp, Kp, Vt, cu_seqlens, perm, gate, softma
                                                      ptr(gate), N, H, D, M, float(softmax_scale), float(beta),
                                                      ptr(O), ptr(ws), nbytes, stream_handle()),
           "moga_group_attention_unpermute_vt")
+    return O
+
+
+def moga_group_attention_unpermute_vtq(Q, Kp, Vt, cu_seqlens, perm, gate, softmax_scale=0.0, beta=0.0, O=None,
+                                       ws=None):
+    """moga_group_attention_unpermute_vt with Q in original token order (read
+    through perm inside the kernel); Kp and Vt from moga_permute_vt."""
+    _need(Q, "Q", BF16, 3)
+    N, H, D = Q.shape
+    _need(Kp, "Kp", BF16, 3, Q.shape)
+    _need(Vt, "Vt", BF16, 3, (H, D, moga_vt_row_length(N)))
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _need(perm, "perm", torch.int32, 1, (N,))
+    _need(gate, "gate", torch.float32, 1, (N,))
+    M = cu_seqlens.shape[0] - 1
+    if O is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs an existing O")
+        O = torch.empty_like(Q)
+    _need(O, "O", BF16, 3, Q.shape)
+    ws, nbytes = _workspace(MOGA_OP_GROUP_ATTENTION, N, M, H, D, ws, Q.device)
+    check(_lib.LIB.moga_group_attention_unpermute_vtq(ptr(Q), ptr(Kp), ptr(Vt), ptr(cu_seqlens), ptr(perm),
+                                                      ptr(gate), N, H, D, M, float(softmax_scale), float(beta),
+                                                      ptr(O), ptr(ws), nbytes, stream_handle()),
+          "moga_group_attention_unpermute_vtq")
     return O
 
 
@@ -322,9 +352,12 @@ class MogaForward:
     calls back to back on the current stream and allocates nothing.
 
     ``path`` selects how the group attention meets the permutation:
-      "fused_vt" (default): gathered Q/K copies and V gathered transposed per
-        head, attention with the gated unpermute in its epilogue
-        (moga_permute_vt, moga_group_attention_unpermute_vt; N <= 2^23 - 128);
+      "fused_vtq" (default): a gathered K copy and V gathered transposed per
+        head; the attention reads each query row through perm and applies
+        the gated unpermute in its epilogue (moga_permute_vt without Q,
+        moga_group_attention_unpermute_vtq; N <= 2^23 - 128);
+      "fused_vt": as "fused_vtq" with a gathered Q copy
+        (moga_group_attention_unpermute_vt);
       "fused_epilogue": as "fused_vt" with V in row layout
         (moga_permute, moga_group_attention_unpermute);
       "gather_on_load": sort only, then moga_group_attention_fused reads
@@ -340,14 +373,14 @@ class MogaForward:
     ``shot_start`` the pass computes the visual attention output of the STGA
     section: the mean of MoGA, shot-aware STGA and per-frame attention."""
 
-    PATHS = ("fused_vt", "fused_epilogue", "gather_on_load", "separate")
+    PATHS = ("fused_vtq", "fused_vt", "fused_epilogue", "gather_on_load", "separate")
     VT_MAX_TOKENS = (1 << 23) - 128
 
-    def __init__(self, N, d_model, H, D, M, device, stga=None, path="fused_vt"):
+    def __init__(self, N, d_model, H, D, M, device, stga=None, path="fused_vtq"):
         if path not in self.PATHS:
             raise ValueError(f"path must be one of {self.PATHS}")
-        if path == "fused_vt" and N > self.VT_MAX_TOKENS:
-            raise ValueError(f"path 'fused_vt' takes at most {self.VT_MAX_TOKENS} tokens; use 'fused_epilogue'")
+        if path in ("fused_vt", "fused_vtq") and N > self.VT_MAX_TOKENS:
+            raise ValueError(f"path '{path}' takes at most {self.VT_MAX_TOKENS} tokens; use 'fused_epilogue'")
         self.N, self.d_model, self.H, self.D, self.M, self.stga = N, d_model, H, D, M, stga
         self.path = path
         e = lambda *s, dt=BF16: torch.empty(*s, dtype=dt, device=device)  # noqa: E731
@@ -357,8 +390,10 @@ class MogaForward:
         copies = path != "gather_on_load"
         self.Qp, self.Kp, self.Vp = (e(N, H, D) if copies else None for _ in range(3))
         self.Vt = None
-        if path == "fused_vt":
+        if path in ("fused_vt", "fused_vtq"):
             self.Vp, self.Vt = None, e(H, D, moga_vt_row_length(N))
+        if path == "fused_vtq":
+            self.Qp = None
         self.Op = e(N, H, D) if path == "separate" else None
         self.perm = e(N, dt=torch.int32)
         self.cu_seqlens = e(M + 1, dt=torch.int32)
@@ -386,6 +421,11 @@ class MogaForward:
                             self.max_seqlen, self.ws_perm)
             moga_group_attention_unpermute_vt(self.Qp, self.Kp, self.Vt, self.cu_seqlens, self.perm, self.gate,
                                               softmax_scale, 0.0, self.O, self.ws_attn)
+        elif self.path == "fused_vtq":
+            moga_permute_vt(self.group_id, self.M, None, K, V, None, self.Kp, self.Vt, self.perm, self.cu_seqlens,
+                            self.max_seqlen, self.ws_perm)
+            moga_group_attention_unpermute_vtq(Q, self.Kp, self.Vt, self.cu_seqlens, self.perm, self.gate,
+                                               softmax_scale, 0.0, self.O, self.ws_attn)
         else:
             moga_permute(self.group_id, self.M, Q, K, V, self.Qp, self.Kp, self.Vp, self.perm, self.cu_seqlens,
                          self.max_seqlen, self.ws_perm)

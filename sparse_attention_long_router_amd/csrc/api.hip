@@ -38,4 +38,5 @@ extern "C" const char* moga_strerror(int32_t status) {
 
 // 0.2.0: shot-aware STGA, gather on load, backward pass
 // 0.3.0: transposed-V gather and attention (moga_permute_vt, moga_group_attention_unpermute_vt)
-extern "C" int32_t moga_version(void) { return 300; }
+// 0.3.1: queries read through perm (moga_group_attention_unpermute_vtq; moga_permute_vt without Q)
+extern "C" int32_t moga_version(void) { return 301; }

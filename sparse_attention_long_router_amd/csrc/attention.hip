@@ -109,7 +109,7 @@ struct MogaRows {
 // P V product is then one 16-byte LDS read instead of two transposing reads.
 struct MogaVtRows {
   static constexpr bool kIndirect = false;
-  static constexpr bool kContiguous = true;
+  [[maybe_unused]] static constexpr bool kContiguous = true;  // as MogaRows; the kVt path takes precedence
   static constexpr bool kTable = false;
   static constexpr bool kVt = true;
   MogaRows base;
@@ -117,6 +117,14 @@ struct MogaVtRows {
   __device__ __forceinline__ bool decode(int item, Work& w) const { return base.decode(item, w); }
   __device__ __forceinline__ int64_t row(const Work& w, int i) const { return w.row0 + i; }
   __device__ __forceinline__ int64_t key(const Work& w, int i) const { return w.row0 + i; }
+};
+
+// MogaVtRows with the queries read in original token order: query i of a
+// group is token perm[row0 + i] of the unpermuted Q, so only K and V^T are
+// gathered.  The output row is that same token (kEpiGatedInPlace).
+struct MogaVtQRows : MogaVtRows {
+  const int32_t* perm;
+  __device__ __forceinline__ int64_t row(const Work& w, int i) const { return perm[w.row0 + i]; }
 };
 
 // Learned groups read in place (gather on load): permuted row j of a group is
@@ -981,6 +989,32 @@ extern "C" int moga_group_attention_unpermute_vt(const void* Qp, const void* Kp,
   const Epilogue epi{1.f, beta, perm, gate, nullptr, 0};
   if (D == 128) return launch_attn<128, MogaVtRows, kEpiGated>(Qp, Kp, Vt, O, (int64_t)H * D, scale, epi, rows, bound, st);
   return launch_attn<64, MogaVtRows, kEpiGated>(Qp, Kp, Vt, O, (int64_t)H * D, scale, epi, rows, bound, st);
+}
+
+extern "C" int moga_group_attention_unpermute_vtq(const void* Q, const void* Kp, const void* Vt,
+                                                  const int32_t* cu_seqlens, const int32_t* perm, const float* gate,
+                                                  int64_t N, int32_t H, int32_t D, int32_t M, float softmax_scale,
+                                                  float beta, void* O, void* ws, size_t ws_bytes, void* stream) {
+  using namespace moga;
+  if (!Q || !Kp || !Vt || !cu_seqlens || !perm || !gate || !O) return MOGA_ERR_NULL;
+  if (N < 1 || N >= (int64_t(1) << 31) || M < 1 || H < 1 || D < 1) return MOGA_ERR_SHAPE;
+  if (M > kMaxGroups || !valid_head_dims(H, D) || N > kVtMaxTokens) return MOGA_ERR_UNSUPPORTED;
+  const size_t need = moga_workspace_bytes(MOGA_OP_GROUP_ATTENTION, N, M, H, D);
+  if (!ws || ws_bytes < need) return MOGA_ERR_WORKSPACE;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
+  hipStream_t st = as_stream(stream);
+  auto* sched = static_cast<AttnSchedule*>(ws);
+  schedule_kernel<<<1, kWave, 0, st>>>(cu_seqlens, M, H, sched);
+  MOGA_LAUNCH_CHECK();
+  MogaVtQRows rows;
+  rows.base = MogaRows{cu_seqlens, sched, M, H};
+  rows.ldv = vt_row_length(N);
+  rows.perm = perm;
+  const int64_t bound = (ceil_div(N, kBM) + M) * H;
+  const Epilogue epi{1.f, beta, nullptr, gate, nullptr, 0};
+  if (D == 128)
+    return launch_attn<128, MogaVtQRows, kEpiGatedInPlace>(Q, Kp, Vt, O, (int64_t)H * D, scale, epi, rows, bound, st);
+  return launch_attn<64, MogaVtQRows, kEpiGatedInPlace>(Q, Kp, Vt, O, (int64_t)H * D, scale, epi, rows, bound, st);
 }
 
 extern "C" size_t moga_stga_shot_workspace_bytes(int32_t T, int32_t n_shots, int32_t win_t) {

@@ -16,10 +16,10 @@
 //                   are ordered through LDS counts -> perm[base + rank] = n
 //   gather_kernel   Qp/Kp/Vp[j] = Q/K/V[perm[j]], whole H*D rows, 16-byte
 //                   lanes, one wave per row copy (HBM-bound stream)
-// moga_permute_vt runs the same sort, gathers only Q and K as rows and
-// writes V transposed per head (gather_vt_kernel): Vt[h][d][j], the layout
-// whose 64-key tiles the attention reads with one 16-byte LDS read per MFMA
-// operand.
+// moga_permute_vt runs the same sort, gathers only Q and K as rows (or K
+// alone, for an attention that reads Q through perm) and writes V transposed
+// per head (gather_vt_kernel): Vt[h][d][j], the layout whose 64-key tiles the
+// attention reads with one 16-byte LDS read per MFMA operand.
 #include "moga_internal.h"
 
 namespace moga {
@@ -135,7 +135,7 @@ constexpr int kGatherBatch = 3;  // 64-lane chunk steps loaded before any store
 // wave copies one row of each tensor; all loads of a batch (three 1 KB
 // contiguous pieces per tensor, the whole row at H*D = 1536) are in flight
 // before the first store, which measured 4% faster than interleaving them.
-template <bool kWithV>
+template <bool kWithQ, bool kWithV>
 __global__ __launch_bounds__(kGatherWaves * kWave) void gather_kernel(
     const int32_t* __restrict__ perm, int64_t N, int chunks, const u32x4* __restrict__ Q,
     const u32x4* __restrict__ K, const u32x4* __restrict__ V, u32x4* __restrict__ Qp, u32x4* __restrict__ Kp,
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(kGatherWaves * kWave) void gather_kernel(
     for (int u = 0; u < kGatherBatch; ++u) {
       const int c = c0 + u * kWave + lane;
       if (c < chunks) {
-        a[u] = __builtin_nontemporal_load(Q + src + c);
+        if constexpr (kWithQ) a[u] = __builtin_nontemporal_load(Q + src + c);
         b[u] = __builtin_nontemporal_load(K + src + c);
         if constexpr (kWithV) d[u] = __builtin_nontemporal_load(V + src + c);
       }
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kGatherWaves * kWave) void gather_kernel(
     for (int u = 0; u < kGatherBatch; ++u) {
       const int c = c0 + u * kWave + lane;
       if (c < chunks) {
-        __builtin_nontemporal_store(a[u], Qp + dst + c);
+        if constexpr (kWithQ) __builtin_nontemporal_store(a[u], Qp + dst + c);
         __builtin_nontemporal_store(b[u], Kp + dst + c);
         if constexpr (kWithV) __builtin_nontemporal_store(d[u], Vp + dst + c);
       }
@@ -240,7 +240,7 @@ extern "C" int moga_permute(const int32_t* group_id, const void* Q, const void* 
   if (all_rows) {
     const int chunks = H * D / 8;
     const int64_t blocks = ceil_div(N, kGatherWaves);
-    gather_kernel<true><<<dim3((unsigned)blocks), kGatherWaves * kWave, 0, st>>>(
+    gather_kernel<true, true><<<dim3((unsigned)blocks), kGatherWaves * kWave, 0, st>>>(
         perm, N, chunks, static_cast<const u32x4*>(Q), static_cast<const u32x4*>(K), static_cast<const u32x4*>(V),
         static_cast<u32x4*>(Qp), static_cast<u32x4*>(Kp), static_cast<u32x4*>(Vp));
     MOGA_LAUNCH_CHECK();
@@ -252,7 +252,8 @@ extern "C" int moga_permute_vt(const int32_t* group_id, const void* Q, const voi
                                int32_t H, int32_t D, int32_t M, void* Qp, void* Kp, void* Vt, int32_t* perm,
                                int32_t* cu_seqlens, int32_t* max_seqlen, void* ws, size_t ws_bytes, void* stream) {
   using namespace moga;
-  if (!group_id || !perm || !cu_seqlens || !max_seqlen || !Q || !K || !V || !Qp || !Kp || !Vt) return MOGA_ERR_NULL;
+  if (!group_id || !perm || !cu_seqlens || !max_seqlen || !K || !V || !Kp || !Vt) return MOGA_ERR_NULL;
+  if (!Q != !Qp) return MOGA_ERR_NULL;  // Q is gathered only when both are given
   if (N < 1 || N >= (int64_t(1) << 31) || M < 1 || H < 1 || D < 1) return MOGA_ERR_SHAPE;
   if (M > kMaxGroups || !valid_head_dims(H, D) || N > kVtMaxTokens) return MOGA_ERR_UNSUPPORTED;
   // the sort, as moga_permute without row copies
@@ -261,9 +262,14 @@ extern "C" int moga_permute_vt(const int32_t* group_id, const void* Q, const voi
   if (rc != MOGA_OK) return rc;
   hipStream_t st = as_stream(stream);
   const int chunks = H * D / 8;
-  gather_kernel<false><<<dim3((unsigned)ceil_div(N, kGatherWaves)), kGatherWaves * kWave, 0, st>>>(
-      perm, N, chunks, static_cast<const u32x4*>(Q), static_cast<const u32x4*>(K), nullptr,
-      static_cast<u32x4*>(Qp), static_cast<u32x4*>(Kp), nullptr);
+  const dim3 rows_grid((unsigned)ceil_div(N, kGatherWaves));
+  if (Q)
+    gather_kernel<true, false><<<rows_grid, kGatherWaves * kWave, 0, st>>>(
+        perm, N, chunks, static_cast<const u32x4*>(Q), static_cast<const u32x4*>(K), nullptr,
+        static_cast<u32x4*>(Qp), static_cast<u32x4*>(Kp), nullptr);
+  else
+    gather_kernel<false, false><<<rows_grid, kGatherWaves * kWave, 0, st>>>(
+        perm, N, chunks, nullptr, static_cast<const u32x4*>(K), nullptr, nullptr, static_cast<u32x4*>(Kp), nullptr);
   MOGA_LAUNCH_CHECK();
   const int64_t ldv = vt_row_length(N);
   const dim3 grid((unsigned)(ldv / kVtTile), (unsigned)H);

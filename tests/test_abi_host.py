@@ -33,7 +33,7 @@ def declared_symbols():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(lib, n), n
     from sparse_attention_long_router_amd import _lib
@@ -122,7 +122,9 @@ def test_transposed_v_argument_errors(lib):
     nbp = lib.moga_workspace_bytes(1, 100, 4, 2, 128)
     pargs = [FAKE, FAKE, FAKE, FAKE, 100, 2, 128, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, nbp, None]
     assert p(None, *pargs[1:]) == ENULL                    # group_id
-    assert p(*pargs[:3], None, *pargs[4:]) == ENULL        # V: every row tensor is required
+    assert p(*pargs[:3], None, *pargs[4:]) == ENULL        # V
+    assert p(*pargs[:1], None, *pargs[2:]) == ENULL        # Q without Qp
+    assert p(*pargs[:8], None, *pargs[9:]) == ENULL        # Qp without Q
     assert p(*pargs[:10], None, *pargs[11:]) == ENULL      # Vt
     assert p(*pargs[:4], 0, *pargs[5:]) == ESHAPE          # N
     assert p(*pargs[:6], 96, *pargs[7:]) == EUNSUP         # D
@@ -135,6 +137,21 @@ def test_transposed_v_argument_errors(lib):
     assert a(*args[:2], None, *args[3:]) == ENULL          # Vt
     assert a(*args[:5], None, *args[6:]) == ENULL          # gate
     assert a(*args[:6], 0, *args[7:]) == ESHAPE            # N
+    assert a(*args[:8], 48, *args[9:]) == EUNSUP           # D
+    assert a(*args[:6], (1 << 23) - 127, *args[7:]) == EUNSUP
+    assert a(*args[:13], None, *args[14:]) == EWS
+    assert a(*args[:14], nb - 1, None) == EWS
+
+
+def test_transposed_v_direct_q_argument_errors(lib):
+    a = lib.moga_group_attention_unpermute_vtq
+    nb = lib.moga_workspace_bytes(2, 100, 4, 2, 128)
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 100, 2, 128, 4, 0.0, 0.0, FAKE, FAKE, nb, None]
+    assert a(None, *args[1:]) == ENULL                     # Q
+    assert a(*args[:4], None, *args[5:]) == ENULL          # perm
+    assert a(*args[:12], None, *args[13:]) == ENULL        # O
+    assert a(*args[:6], 0, *args[7:]) == ESHAPE            # N
+    assert a(*args[:9], 65, *args[10:]) == EUNSUP          # M > 64
     assert a(*args[:8], 48, *args[9:]) == EUNSUP           # D
     assert a(*args[:6], (1 << 23) - 127, *args[7:]) == EUNSUP
     assert a(*args[:13], None, *args[14:]) == EWS

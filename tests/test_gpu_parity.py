@@ -81,6 +81,13 @@ def _full_check(moga, inp, bias=None, label=""):
     Ot = moga.moga_group_attention_unpermute_vt(pv["Qp"], pv["Kp"], pv["Vt"], pv["cu_seqlens"], pv["perm"], gate)
     torch.cuda.synchronize()
     assert_output_close(_np(Ot), ref["O"], "O (transposed V)")
+    # without the Q copy: the attention reads query rows through perm
+    pq = moga.moga_permute_vt(gid, M, None, K, V)
+    assert pq["Qp"] is None
+    assert torch.equal(pq["Kp"], pv["Kp"]) and torch.equal(pq["Vt"], pv["Vt"])
+    Oq = moga.moga_group_attention_unpermute_vtq(Q, pq["Kp"], pq["Vt"], pq["cu_seqlens"], pq["perm"], gate)
+    torch.cuda.synchronize()
+    assert torch.equal(Oq, Ot)   # same query values, same arithmetic
     print(f"[parity] {label} Op {e_attn} O {e_out}", flush=True)
     return gid, gate, p, Op, O, ref
 
@@ -234,6 +241,7 @@ def test_stga_shot(moga, T, Hs, Ws, shots, win_t, th, tw, aug, H, D, alpha, beta
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("name,path", [("wan13b_21f", "fused_vt"), ("clip30s_122f", "fused_vt"),
+                                       ("clip30s_122f", "fused_vtq"), ("wan13b_21f", "fused_vtq"),
                                        ("clip30s_122f", "fused_epilogue"), ("clip30s_122f", "gather_on_load"),
                                        ("clip30s_122f", "separate"), ("wan14b_122f", "fused_vt"),
                                        ("minute_372f", "fused_vt"), ("minute_372f", "fused_epilogue"),
