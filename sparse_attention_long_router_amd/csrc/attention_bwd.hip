@@ -203,7 +203,7 @@ __device__ __forceinline__ bool decode(const AttnSchedule* sched, const int32_t*
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: 4 waves x 32 keys, queries streamed in tiles of 64
+// dK, dV: 4 waves x 32 keys, queries streamed in tiles of kTileQ (128)
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kDkvWaves * kWave) void dkdv_kernel(
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kDkvWaves * kWave) void dkdv_kernel(
   const int ntiles = (w.len + kTile - 1) / kTile;
   const float c2 = scale * 1.4426950408889634f;  // scores to log2 units
 
-  // tile t: Q and dA rows, lse and delta of queries t*64 .. t*64+63
+  // tile t: Q and dA rows, lse and delta of queries t*kTile .. t*kTile+kTile-1
   auto issue = [&](int buf, int t) {
     const int64_t first = (int64_t)w.row0 + (int64_t)t * kTile;
     const int64_t n = w.len - (int64_t)t * kTile;
@@ -312,7 +312,7 @@ __global__ __launch_bounds__(kDkvWaves * kWave) void dkdv_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dQ: 8 waves x 32 queries, keys and values streamed in tiles of 64
+// dQ: 8 waves x 32 queries, keys and values streamed in tiles of kTileK (128)
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kDqWaves * kWave) void dq_kernel(
