@@ -100,11 +100,21 @@ def cpu_baseline(inp, wl, counts, rows_per_group):
 
     import oracle
     from workloads.gen import sample_rows, to_numpy_f32
+    blas = "unknown BLAS"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+        info = threadpool_info()
+        threads = max([int(i.get("num_threads", 1)) for i in info] or [1])
+        blas = ", ".join(sorted({f"{i.get('internal_api', '?')} ({i.get('threading_layer', '?')})"
+                                 for i in info if i.get("user_api") == "blas"})) or blas
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
+    cpu = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next(line.split(":", 1)[1].strip() for line in f if line.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
 
     X, Wr, Q, K, V = (to_numpy_f32(inp[k]) for k in ("X", "Wr", "Q", "K", "V"))
     t0 = time.perf_counter()
@@ -128,7 +138,8 @@ def cpu_baseline(inp, wl, counts, rows_per_group):
         "sample": (f"route + permute over all {wl.N} tokens ({t_route:.2f} s); attention of {rows.size} "
                    f"sampled query rows (first, last and {rows_per_group} random per group) x {wl.H} heads "
                    f"({t_attn:.2f} s, {sample_flops / 1e9:.1f} GFLOP), extrapolated by FLOPs to the full step "
-                   f"({t_full:.1f} s); float64 NumPy, {len(os.sched_getaffinity(0))} cores visible"),
+                   f"({t_full:.1f} s); float64 NumPy on {blas}, {threads} BLAS threads, "
+                   f"{len(os.sched_getaffinity(0))} cores visible, {cpu}"),
     }
 
 

@@ -176,6 +176,22 @@ def test_gather_on_load_accumulates(moga):
     assert_output_close(_np(O), ref["O"] + 0.5 * _np(inp["V"]), "gather-on-load O + 0.5 V")
 
 
+@pytest.mark.parametrize("D", [128, 64])
+def test_transposed_v_paths_accumulate(moga, D):
+    inp = _inputs("wan13b_21f", N=2600, H=2, D=D, M=5, d_model=256)
+    gid, gate = moga.moga_route(inp["X"], inp["Wr"])
+    pv = moga.moga_permute_vt(gid, 5, inp["Q"], inp["K"], inp["V"])
+    pq = moga.moga_permute_vt(gid, 5, None, inp["K"], inp["V"])
+    Ot = moga.moga_group_attention_unpermute_vt(pv["Qp"], pv["Kp"], pv["Vt"], pv["cu_seqlens"], pv["perm"], gate,
+                                                beta=0.5, O=inp["V"].clone())
+    Oq = moga.moga_group_attention_unpermute_vtq(inp["Q"], pq["Kp"], pq["Vt"], pq["cu_seqlens"], pq["perm"], gate,
+                                                 beta=0.5, O=inp["V"].clone())
+    torch.cuda.synchronize()
+    ref = oracle.moga_forward(*(_np(inp[k]) for k in ("X", "Wr", "Q", "K", "V")), 5)
+    assert_output_close(_np(Oq), ref["O"] + 0.5 * _np(inp["V"]), "transposed-V, queries through perm: O + 0.5 V")
+    assert torch.equal(Oq, Ot)
+
+
 def test_unpermute_accumulate(moga):
     inp = _inputs("wan13b_21f", N=2500, H=2, D=64, M=5, d_model=128)
     gid, gate = moga.moga_route(inp["X"], inp["Wr"])
