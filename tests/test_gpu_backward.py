@@ -84,6 +84,17 @@ def test_backward_shapes(moga, N, H, D, M, d):
     _check(moga, *_case("wan13b_21f", seed=77, N=N, H=H, D=D, M=M, d_model=d), label=f"shape {N, H, D, M, d}")
 
 
+def _sweep_shapes(seed, count):
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(1, 6001)), int(rng.integers(1, 4)), int(rng.choice([64, 128])),
+             int(rng.integers(1, 33)), int(rng.choice([64, 128]))) for _ in range(count)]
+
+
+@pytest.mark.parametrize("N,H,D,M,d", _sweep_shapes(2025, 5))
+def test_backward_shape_sweep(moga, N, H, D, M, d):
+    _check(moga, *_case("wan13b_21f", seed=N + M, N=N, H=H, D=D, M=M, d_model=d), label=f"sweep {N, H, D, M, d}")
+
+
 def test_backward_with_bias(moga):
     X, Wr, Q, K, V, dO, b = _case("wan13b_21f", seed=78, bias=True, N=1500, H=2, D=128, M=6, d_model=128)
     _check(moga, X, Wr, Q, K, V, dO, b, label="bias")

@@ -109,6 +109,23 @@ def test_shapes(moga, N, H, D, M):
     _full_check(moga, _inputs("wan13b_21f", N=N, H=H, D=D, M=M, d_model=256), label=f"shape{N}")
 
 
+def _sweep_shapes(seed, count):
+    """Seeded random shapes: token counts from 1 to 9000, 1-4 heads of 64 or
+    128, 1-64 groups, small model widths."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        N = int(rng.choice([int(rng.integers(1, 200)), int(rng.integers(200, 9001))]))
+        out.append((N, int(rng.integers(1, 5)), int(rng.choice([64, 128])), int(rng.integers(1, 65)),
+                    int(rng.choice([64, 128, 256]))))
+    return out
+
+
+@pytest.mark.parametrize("N,H,D,M,d", _sweep_shapes(2024, 10))
+def test_shape_sweep(moga, N, H, D, M, d):
+    _full_check(moga, _inputs("wan13b_21f", seed=N + M, N=N, H=H, D=D, M=M, d_model=d), label=f"sweep{N, H, D, M}")
+
+
 def test_skewed_with_bias_and_empty_groups(moga):
     inp = _inputs("clip30s_122f", N=5000, H=2, D=128, M=6, d_model=512)
     # bias pushes most tokens into group 2 and empties group 5
