@@ -62,6 +62,8 @@ SIGNATURES = {
 
 
 BUILD_HINT = "run `python sparse_attention_long_router_amd/build.py`"
+# moga_version() of the sources this binding matches (csrc/api.hip)
+EXPECTED_VERSION = 301
 
 
 def _load():
@@ -75,6 +77,10 @@ def _load():
             raise ImportError(f"{LIB_PATH} lacks {name} (stale build); {BUILD_HINT}") from None
         fn.restype = res
         fn.argtypes = args
+    got = int(lib.moga_version())
+    if got != EXPECTED_VERSION:
+        raise ImportError(f"{LIB_PATH} is version {got}, the binding expects {EXPECTED_VERSION} (stale build); "
+                          f"{BUILD_HINT}")
     return lib
 
 

@@ -47,6 +47,16 @@ def test_strerror_and_version(lib):
     assert lib.moga_version() >= 100
 
 
+def test_binding_matches_library_version():
+    """The binding refuses a library built from other sources (a stale build)."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    api = open(os.path.join(root, "sparse_attention_long_router_amd", "csrc", "api.hip")).read()
+    src_version = int(re.search(r"moga_version\(void\) \{ return (\d+); \}", api).group(1))
+    from sparse_attention_long_router_amd import _lib
+    assert _lib.EXPECTED_VERSION == src_version
+    assert _lib.LIB.moga_version() == src_version
+
+
 def test_workspace_sizes(lib):
     ws = lib.moga_workspace_bytes
     assert ws(0, 1000, 4, 2, 64) == 0                      # route needs none
