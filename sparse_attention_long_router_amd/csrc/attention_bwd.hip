@@ -110,10 +110,11 @@ __device__ __forceinline__ f32x16 rows_mma(const uint16_t* T, int rbase, const b
 // the dq kernel at 190k tokens), while the second wave on the SIMD covers the
 // LDS latency this version exposes.
 template <int D, int kSwz>
-__device__ __forceinline__ f32x16 rows_mma_lean(const uint16_t* T, int rbase, const bf16x8 (&b)[D / 16], int lane) {
+__device__ __forceinline__ f32x16 rows_mma_lean(const uint16_t* T, int rbase, const bf16x8 (&b)[D / 16], int lane,
+                                                f32x16 c0 = f32x16{}) {
   constexpr int CPR = D / 8;
   const int hh = lane >> 5, row = rbase + (lane & 31);
-  f32x16 c = {};
+  f32x16 c = c0;
 #pragma unroll
   for (int st = 0; st < D / 16; ++st)
     c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -355,6 +356,9 @@ __global__ __launch_bounds__(kDqWaves * kWave) void dq_kernel(
   f32x16 dq[DBLK];
 #pragma unroll
   for (int db = 0; db < DBLK; ++db) dq[db] = f32x16{};
+  f32x16 ndl;  // -delta of this lane's query: the dP^T accumulator starts there and yields dP^T - delta
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ndl[r] = -dl;
 
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
@@ -368,10 +372,10 @@ __global__ __launch_bounds__(kDqWaves * kWave) void dq_kernel(
       f32x16 s, dp;
       if constexpr (D == 128) {
         s = rows_mma_lean<D, kBoth>(Ks[buf], kb * 32, qf, lane);
-        dp = rows_mma_lean<D, kRowsOnly>(Vs[buf], kb * 32, af, lane);
+        dp = rows_mma_lean<D, kRowsOnly>(Vs[buf], kb * 32, af, lane, ndl);
       } else {
         s = rows_mma<D, kBoth>(Ks[buf], kb * 32, qf, lane);
-        dp = rows_mma<D, kRowsOnly>(Vs[buf], kb * 32, af, lane);
+        dp = rows_mma<D, kRowsOnly>(Vs[buf], kb * 32, af, lane, ndl);
       }
       bf16x8 sb[2];
 #pragma unroll
@@ -382,7 +386,7 @@ __global__ __launch_bounds__(kDqWaves * kWave) void dq_kernel(
         // where a very negative log-sum-exp would overflow p and turn their
         // zero product into inf * 0; clamped, p stays finite and they add 0.
         const float p = __builtin_amdgcn_exp2f(fminf(fmaf(s[r], c2, -l2), 0.5f));
-        sb[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dl));
+        sb[r >> 3][r & 7] = (__bf16)(p * dp[r]);
       }
       tr_mma<D, kBoth>(Ks[buf], kb * 32, sb, lane, dq);  // dQ^T += K^T dS^T
     }
