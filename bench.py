@@ -69,6 +69,25 @@ def calibrate_copy(mib):
     print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}), flush=True)
 
 
+def copy_rate_gbs(stream, mib=1024, reps=5):
+    """Read + write bytes per second of a plain device-to-device copy (the
+    practical ceiling of a streaming kernel), timed with HIP events."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").random_(0, 255)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    rate = 2.0 * n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    return rate
+
+
 def attn_flops(counts, H, D):
     return 4.0 * H * D * float(sum(int(c) ** 2 for c in counts))
 
@@ -332,6 +351,9 @@ def main():
         hbm["permute"] = wl.N * (12 * wl.H * wl.D + 16)
     out["hbm_gbs"] = {k: round(b / (breakdown[k] * 1e-3) / 1e9, 1) for k, b in hbm.items()}
     out["hbm_frac"] = {k: round(v / PEAK_HBM_GBS, 4) for k, v in out["hbm_gbs"].items()}
+    copy_gbs = copy_rate_gbs(stream)
+    out["hbm_copy_gbs"] = round(copy_gbs, 1)  # measured device-to-device copy, read + write bytes
+    out["hbm_frac_of_copy"] = {k: round(v / copy_gbs, 4) for k, v in out["hbm_gbs"].items()}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, wl, counts, args.cpu_rows)
     print(json.dumps(out), flush=True)
