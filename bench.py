@@ -40,7 +40,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_group_attention_clip30s_1
 ATTN_SOURCE = os.path.join(ROOT, "sparse_attention_long_router_amd", "csrc", "attention.hip")
 
 
-def parse():
+def make_parser():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -53,7 +53,11 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=2000, help="sampled query rows per group for the oracle")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of MIB MiB (reference for HBM byte counters)")
-    return ap.parse_args()
+    return ap
+
+
+def parse():
+    return make_parser().parse_args()
 
 
 def calibrate_copy(mib):
