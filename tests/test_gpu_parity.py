@@ -297,7 +297,12 @@ def test_full_size_sampled(moga, name, path):
     np.testing.assert_array_equal(fwd.cu_seqlens.cpu().numpy(), cu_ref)
     assert int(fwd.max_seqlen.item()) == mx_ref
 
-    rows = sample_rows(g_ref, wl.M, per_group=3, seed=wl.seed)
+    rows = sample_rows(g_ref, wl.M, per_group=6, seed=wl.seed)
+    # plus the queries on both sides of the first 32-query wave and 256-query
+    # work-item boundaries of every group (permuted positions 31/32, 255/256)
+    edges = [perm_ref[cu_ref[i] + j] for i in range(wl.M) for j in (31, 32, 255, 256)
+             if cu_ref[i] + j < cu_ref[i + 1]]
+    rows = np.unique(np.concatenate([rows, np.asarray(edges, dtype=np.int64)]))
     Qn, Kn, Vn = _np(Q), _np(K), _np(V)
     want = oracle.moga_output_rows(Xn, Wn, Qn, Kn, Vn, wl.M, rows, routed=(g_ref, gate_ref))
     if wl.stga is not None:
