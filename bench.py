@@ -97,8 +97,16 @@ def attn_flops(counts, H, D):
 
 
 def source_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a C++ source with its comments and blank space removed, so that
+    a change to comments alone does not disown counters taken on the same
+    code (string literals in these kernels hold no comment markers)."""
+    import re
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def traffic_entry(kernel, workload):

@@ -22,8 +22,8 @@
 //   halves share a query and exchange one value with v_permlane32_swap);
 //   softmax in float32 with exp2 and the scale folded into one FMA, against
 //   an exponent offset fixed from each row's first 32 keys (no accumulator
-//   rescaling; a work item whose later scores exceed that offset by 2^32 is
-//   recomputed with exact row maxima);
+//   rescaling; a work item where a row's sum of weights against that offset
+//   reaches 2^64 or overflows is recomputed with exact row maxima);
 //   O^T += V^T P^T with the same MFMA: B = P^T comes straight from the S^T
 //   registers (the k-slot order of an MFMA is free as long as both operands
 //   agree), A = V^T comes from row-major V in LDS through two
@@ -256,9 +256,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 // row's first 32 keys before the key loop and never moves, so the output
 // accumulator is never rescaled and no per-tile row max is needed.  Weights
 // above 1 (later scores above the first keys' max) keep their relative
-// precision in float32 and bf16; only a denominator that reaches 2^kLogLimit
-// (or overflows) could lose the output, and the work item is then recomputed
-// with the exact row max (see attn_kernel).
+// precision in float32 and bf16; only a denominator that reaches kLimit
+// (2^64) or overflows could lose the output, and the work item is then
+// recomputed with the exact row max (see attn_kernel).
 struct RowState {
   float m_ref;  // exponent offset (log2 domain)
   float l;      // this lane's share of the denominator
