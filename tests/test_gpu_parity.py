@@ -126,6 +126,63 @@ def test_shape_sweep(moga, N, H, D, M, d):
     _full_check(moga, _inputs("wan13b_21f", seed=N + M, N=N, H=H, D=D, M=M, d_model=d), label=f"sweep{N, H, D, M}")
 
 
+_GUARD = 4096  # elements after every output that no call may touch
+
+
+def _guarded(shape, dtype):
+    """An output view at the start of a larger buffer; the buffer is filled
+    with NaN (float types) or -7 (integers) so that an unwritten output
+    element or a write past the end shows."""
+    n = int(np.prod(shape))
+    fill = float("nan") if dtype.is_floating_point else -7
+    buf = torch.full((n + _GUARD,), fill, dtype=dtype, device=DEV)
+    return buf[:n].view(shape), buf
+
+
+def _guard_intact(buf, n):
+    g = buf[n:]
+    return bool(torch.isnan(g).all()) if g.dtype.is_floating_point else bool((g == -7).all())
+
+
+@pytest.mark.parametrize("bias_on", [False, True])
+def test_outputs_fully_written_and_guarded(moga, bias_on):
+    """Every output element of the default path's calls is written (no NaN
+    from the poison fill survives, and beta = 0 reads nothing), nothing is
+    written past the end of an output, and with a bias that sends about 90%
+    of the tokens to one group (skew stress) the result still matches."""
+    N, H, D, M = 3001, 2, 128, 5
+    inp = _inputs("wan13b_21f", N=N, H=H, D=D, M=M, d_model=256)
+    X, Wr, Q, K, V = (inp[k] for k in ("X", "Wr", "Q", "K", "V"))
+    bias = torch.tensor([0.0, 0.0, 3.5, 0.0, 0.0], device=DEV) if bias_on else None
+    gid, gbuf = _guarded((N,), torch.int32)
+    gate, gtbuf = _guarded((N,), torch.float32)
+    moga.moga_route(X, Wr, bias, gid, gate)
+    ldv = moga.moga_vt_row_length(N)
+    Kp, kbuf = _guarded((N, H, D), torch.bfloat16)
+    Vt, vbuf = _guarded((H, D, ldv), torch.bfloat16)
+    perm, pbuf = _guarded((N,), torch.int32)
+    cu, cbuf = _guarded((M + 1,), torch.int32)
+    mx, mbuf = _guarded((1,), torch.int32)
+    moga.moga_permute_vt(gid, M, None, K, V, None, Kp, Vt, perm, cu, mx)
+    O, obuf = _guarded((N, H, D), torch.bfloat16)
+    moga.moga_group_attention_unpermute_vtq(Q, Kp, Vt, cu, perm, gate, 0.0, 0.0, O)
+    torch.cuda.synchronize()
+    for name, t, buf in (("group_id", gid, gbuf), ("gate", gate, gtbuf), ("Kp", Kp, kbuf), ("Vt", Vt, vbuf),
+                         ("perm", perm, pbuf), ("cu_seqlens", cu, cbuf), ("max_seqlen", mx, mbuf), ("O", O, obuf)):
+        assert _guard_intact(buf, t.numel()), f"{name}: write past the end"
+        if t.dtype.is_floating_point:
+            assert not torch.isnan(t).any(), f"{name}: elements left unwritten"
+        else:
+            assert not (t == -7).any(), f"{name}: elements left unwritten"
+    counts = np.bincount(gid.cpu().numpy(), minlength=M)
+    if bias_on:
+        assert counts.max() >= 0.85 * N, counts
+    ref = oracle.moga_forward(*(_np(t) for t in (X, Wr, Q, K, V)), M,
+                              bias=None if bias is None else bias.cpu().numpy())
+    np.testing.assert_array_equal(gid.cpu().numpy(), ref["group_id"])
+    assert_output_close(_np(O), ref["O"], "O (poison-filled outputs)")
+
+
 def test_skewed_with_bias_and_empty_groups(moga):
     inp = _inputs("clip30s_122f", N=5000, H=2, D=128, M=6, d_model=512)
     # bias pushes most tokens into group 2 and empties group 5

@@ -622,3 +622,51 @@ def test_pins_catch_planted_mistakes(monkeypatch, name, mutant, checks):
     for check in checks:
         with pytest.raises((AssertionError, IndexError, ValueError)):
             check()
+
+
+# ---------------------------------------------------------------------------
+# Property tests: random sizes, including empty groups, one group holding
+# every token and fewer tokens than a tile
+# ---------------------------------------------------------------------------
+
+from hypothesis import HealthCheck, given, settings  # noqa: E402
+from hypothesis import strategies as st  # noqa: E402
+
+_sizes = st.tuples(st.integers(1, 300), st.integers(1, 64), st.sampled_from([1, 2, 3]), st.sampled_from([64, 128]),
+                   st.integers(0, 2**31 - 1), st.booleans())
+
+
+@settings(max_examples=25, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(_sizes)
+def test_property_forward(case):
+    N, M, H, D, seed, one_group = case
+    r = _rng(seed)
+    d = 16
+    X = r.standard_normal((N, d))
+    Wr = r.standard_normal((M, d)) / math.sqrt(d)
+    b = np.zeros(M)
+    if one_group:
+        b[M - 1] = 1e3                     # every token routed to the last group
+    Q, K, V = (r.standard_normal((N, H, D)) for _ in range(3))
+    out = oracle.moga_forward(X, Wr, Q, K, V, M=M, bias=b)
+    g, perm, cu = out["group_id"], out["perm"], out["cu_seqlens"]
+    # every token in exactly one group; counts add up; empty groups repeat cu
+    assert g.shape == (N,) and g.min() >= 0 and g.max() < M
+    assert cu[0] == 0 and cu[-1] == N and np.all(np.diff(cu) >= 0)
+    np.testing.assert_array_equal(np.diff(cu), np.bincount(g, minlength=M))
+    assert out["max_seqlen"] == np.diff(cu).max()
+    # perm is a bijection, contiguous by group in group order, stable inside
+    np.testing.assert_array_equal(np.sort(perm), np.arange(N))
+    key = g[perm].astype(np.int64) * N + perm
+    assert np.all(np.diff(key) > 0)
+    if one_group:
+        assert np.all(g == M - 1)
+    # the gate is the softmax probability of the chosen group
+    r_logits = X @ Wr.T + b
+    p = np.exp(r_logits - r_logits.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    np.testing.assert_allclose(out["gate"], p[np.arange(N), g], rtol=1e-5)
+    # output: gated attention masked to the token's own group (library routine)
+    mask = g[:, None] == g[None, :]
+    ref = out["gate"].astype(np.float64)[:, None, None] * _sdpa(Q, K, V, mask, scale=1 / math.sqrt(D))
+    np.testing.assert_allclose(out["O"], ref, atol=1e-6)
