@@ -341,7 +341,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded Gaussian-mixture tokens, random-init router and Q/K/V projections)",
-        "config": {"workload": wl.name, "path": args.path, "N": wl.N, "d_model": wl.d_model, "H": wl.H, "D": wl.D, "M": wl.M,
+        "config": {"workload": wl.name, "path": args.path, "N": wl.N, "d_model": wl.d_model, "H": wl.H, "D": wl.D,
+                   "M": wl.M,
+                   "group_sizes": {"min": int(min(counts)), "mean": round(mean, 1), "max": int(max(counts))},
                    "group_max_over_mean": round(max(counts) / mean, 3),
                    "skew_sum_n2_over_uniform": round(sum(c * c for c in counts) / (wl.N * mean), 3),
                    "stga": wl.stga},
