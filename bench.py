@@ -363,6 +363,11 @@ def main():
         hbm["permute"] = wl.N * (8 * wl.H * wl.D + 16)
     elif args.path != "gather_on_load":
         hbm["permute"] = wl.N * (12 * wl.H * wl.D + 16)
+    if wl.stga is not None:  # the STGA branch's own rate (a second MFMA-bound kernel of the step)
+        stga_ms = breakdown["stga"]
+        out["stga"] = {"kernel": "attn_kernel (moga_stga_attention)", "launch_ms": round(stga_ms, 4),
+                       "flops_per_launch": flops_stga, "tflops": round(flops_stga / (stga_ms * 1e-3) / 1e12, 2),
+                       "frac": round(flops_stga / (stga_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     out["hbm_gbs"] = {k: round(b / (breakdown[k] * 1e-3) / 1e9, 1) for k, b in hbm.items()}
     out["hbm_frac"] = {k: round(v / PEAK_HBM_GBS, 4) for k, v in out["hbm_gbs"].items()}
     copy_gbs = copy_rate_gbs(stream)
