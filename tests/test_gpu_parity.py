@@ -5,6 +5,7 @@ must be bit-exact; float32 gates within GATE_RTOL; bf16 outputs within the
 max-abs / mean-abs / relative-Frobenius bars of tests/parity.py.
 """
 
+import dataclasses
 import math
 
 import numpy as np
@@ -330,15 +331,20 @@ def test_stga_shot(moga, T, Hs, Ws, shots, win_t, th, tw, aug, H, D, alpha, beta
 # Full workload sizes, in the launch configuration the benchmark times
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name,path", [("wan13b_21f", "fused_vt"), ("clip30s_122f", "fused_vt"),
-                                       ("clip30s_122f", "fused_vtq"), ("wan13b_21f", "fused_vtq"),
-                                       ("clip30s_122f", "fused_epilogue"), ("clip30s_122f", "gather_on_load"),
-                                       ("clip30s_122f", "separate"), ("wan14b_122f", "fused_vt"),
-                                       ("minute_372f", "fused_vt"), ("minute_372f", "fused_epilogue"),
-                                       ("minute_372f", "gather_on_load")])
-def test_full_size_sampled(moga, name, path):
+@pytest.mark.parametrize("name,path,seed", [("wan13b_21f", "fused_vt", None), ("clip30s_122f", "fused_vt", None),
+                                            ("clip30s_122f", "fused_vtq", None), ("wan13b_21f", "fused_vtq", None),
+                                            ("clip30s_122f", "fused_vtq", 4242),    # another draw of the recipe
+                                            ("clip30s_122f", "fused_epilogue", None),
+                                            ("clip30s_122f", "gather_on_load", None), ("clip30s_122f", "separate", None),
+                                            ("wan14b_122f", "fused_vt", None), ("wan14b_122f", "fused_vtq", None),
+                                            ("minute_372f", "fused_vtq", None), ("minute_372f", "fused_vt", None),
+                                            ("minute_372f", "fused_epilogue", None),
+                                            ("minute_372f", "gather_on_load", None)])
+def test_full_size_sampled(moga, name, path, seed):
     wl = get_workload(name)
-    print(f"[parity] full {name} path={path} N={wl.N} d={wl.d_model} H={wl.H} M={wl.M}", flush=True)
+    if seed is not None:
+        wl = dataclasses.replace(wl, seed=seed)
+    print(f"[parity] full {name} path={path} seed={wl.seed} N={wl.N} d={wl.d_model} H={wl.H} M={wl.M}", flush=True)
     inp = make_inputs(wl, device=DEV)
     X, Wr, Q, K, V = (inp[k] for k in ("X", "Wr", "Q", "K", "V"))
     fwd = moga.MogaForward(wl.N, wl.d_model, wl.H, wl.D, wl.M, DEV, stga=wl.stga, path=path)
