@@ -431,6 +431,18 @@ def test_attention_score_growth(moga, late, label):
     torch.cuda.synchronize()
     ref = oracle.group_attention(_np(Q), _np(K), _np(V), cu.numpy(), 1 / math.sqrt(D))
     assert_output_close(_np(Op), ref, f"Op ({label})")
+    # the same through the transposed-V paths (their own fallback instantiations):
+    # groups [0, 100) and [100, N) sort to the identity permutation, gate 1
+    gid = torch.cat([torch.zeros(100, dtype=torch.int32), torch.ones(N - 100, dtype=torch.int32)]).to(DEV)
+    gate = torch.ones(N, dtype=torch.float32, device=DEV)
+    Qd, Kd, Vd = Q.to(DEV), K.to(DEV), V.to(DEV)
+    pv = moga.moga_permute_vt(gid, 2, Qd, Kd, Vd)
+    assert torch.equal(pv["perm"].cpu(), torch.arange(N, dtype=torch.int32))
+    Ot = moga.moga_group_attention_unpermute_vt(pv["Qp"], pv["Kp"], pv["Vt"], pv["cu_seqlens"], pv["perm"], gate)
+    Oq = moga.moga_group_attention_unpermute_vtq(Qd, pv["Kp"], pv["Vt"], pv["cu_seqlens"], pv["perm"], gate)
+    torch.cuda.synchronize()
+    assert_output_close(_np(Ot), ref, f"O transposed V ({label})")
+    assert torch.equal(Oq, Ot)
 
 
 @pytest.mark.parametrize("name,M", [("tiny", 4), ("clip30s_122f", 16), ("minute_372f", 32)])
