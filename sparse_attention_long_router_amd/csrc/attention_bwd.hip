@@ -104,19 +104,28 @@ __device__ __forceinline__ f32x16 rows_mma(const uint16_t* T, int rbase, const b
   return c;
 }
 
-// rows_mma with each A operand read just before its MFMA.  The dq kernel keeps
-// Q and dA fragments and the dQ accumulators live; reading all eight operands
-// ahead costs 32 more VGPRs and spills (measured 40.1 ms against 33.9 ms for
-// the dq kernel at 190k tokens), while the second wave on the SIMD covers the
-// LDS latency this version exposes.
+// rows_mma with the first half of the A operands read ahead and the rest just
+// before their MFMAs.  The dq kernel keeps Q and dA fragments, the dQ
+// accumulators and -delta live: reading all eight operands ahead needs 32 more
+// VGPRs than it has and spills, reading each one just in time exposes an LDS
+// round trip per MFMA (dq 30.3 ms; this form 29.5 ms, same box), and the
+// second wave on the SIMD covers what latency is left.
 template <int D, int kSwz>
-__device__ __forceinline__ f32x16 rows_mma_lean(const uint16_t* T, int rbase, const bf16x8 (&b)[D / 16], int lane,
+__device__ __forceinline__ f32x16 rows_mma_half(const uint16_t* T, int rbase, const bf16x8 (&b)[D / 16], int lane,
                                                 f32x16 c0 = f32x16{}) {
   constexpr int CPR = D / 8;
+  constexpr int H2 = D / 32;
   const int hh = lane >> 5, row = rbase + (lane & 31);
+  bf16x8 a[H2];
+#pragma unroll
+  for (int st = 0; st < H2; ++st)
+    a[st] = *reinterpret_cast<const bf16x8*>(T + row * D + ((2 * st + hh) ^ swz<kSwz>(row, CPR)) * 8);
+  __builtin_amdgcn_sched_barrier(0);
   f32x16 c = c0;
 #pragma unroll
-  for (int st = 0; st < D / 16; ++st)
+  for (int st = 0; st < H2; ++st) c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[st], b[st], c, 0, 0, 0);
+#pragma unroll
+  for (int st = H2; st < D / 16; ++st)
     c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
         *reinterpret_cast<const bf16x8*>(T + row * D + ((2 * st + hh) ^ swz<kSwz>(row, CPR)) * 8), b[st], c, 0, 0, 0);
   return c;
@@ -368,11 +377,11 @@ __global__ __launch_bounds__(kDqWaves * kWave) void dq_kernel(
 #pragma unroll
     for (int kb = 0; kb < kTile / 32; ++kb) {
       // S^T[key][query] and dP^T[key][query]; at D = 64 the preloading form
-      // keeps three waves per SIMD, at D = 128 the lean one avoids spills
+      // keeps three waves per SIMD, at D = 128 the half-preloading one fits
       f32x16 s, dp;
       if constexpr (D == 128) {
-        s = rows_mma_lean<D, kBoth>(Ks[buf], kb * 32, qf, lane);
-        dp = rows_mma_lean<D, kRowsOnly>(Vs[buf], kb * 32, af, lane, ndl);
+        s = rows_mma_half<D, kBoth>(Ks[buf], kb * 32, qf, lane);
+        dp = rows_mma_half<D, kRowsOnly>(Vs[buf], kb * 32, af, lane, ndl);
       } else {
         s = rows_mma<D, kBoth>(Ks[buf], kb * 32, qf, lane);
         dp = rows_mma<D, kRowsOnly>(Vs[buf], kb * 32, af, lane, ndl);
