@@ -298,18 +298,20 @@ __global__ __launch_bounds__(kDkvWaves * kWave) void dkdv_kernel(
       const f32x16 s = rows_mma<D, kBoth>(Qt, qb * 32, kf, lane);       // S[query][key]
       const f32x16 dp = rows_mma<D, kBoth>(At, qb * 32, vf, lane, nd);  // dP[query][key] - delta[query]
       bf16x8 pb[2], sb[2];
+      float pf[16];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Ls[buf][qb * 32 + 8 * g + 4 * hh]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * g + i;
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l4[i]));
-          pb[r >> 3][r & 7] = (__bf16)p;
-          sb[r >> 3][r & 7] = (__bf16)(p * dp[r]);
+          pf[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l4[i]));
+          pb[r >> 3][r & 7] = (__bf16)pf[r];
         }
       }
       tr_mma<D, kBoth>(At, qb * 32, pb, lane, dv);  // dV^T += dA^T P
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sb[r >> 3][r & 7] = (__bf16)(pf[r] * dp[r]);
       tr_mma<D, kBoth>(Qt, qb * 32, sb, lane, dk);  // dK^T += Q^T dS
     }
   }
