@@ -64,6 +64,7 @@ constexpr int kChan = 256;      // channels per block (one per thread)
 constexpr int kDxTokens = 64;   // tokens per dX block
 constexpr int kDwTokens = 1024; // tokens per dW_r partial block
 constexpr int kDwStage = 128;   // dlogits rows staged in LDS at a time
+constexpr int kDwUnroll = 16;   // X rows loaded ahead of their FMAs
 
 // dX[n][c] = sum_j dlogits[n][j] * W_r[j][c]: a thread owns channel c and
 // keeps W_r[:, c] in registers; the block's dlogits rows sit in LDS.
@@ -101,17 +102,31 @@ __global__ __launch_bounds__(kChan) void router_dx_kernel(const float* __restric
 
 // Partial dW_r (and db) of one block of kDwTokens tokens:
 // part[blk][j][c] = sum_n dlogits[n][j] * X[n][c], dbp[blk][j] = sum_n dlogits[n][j].
+// A thread owns CPT consecutive channels (one 2*CPT-byte load of X per token)
+// and keeps 16*MB*CPT accumulators; the block's dlogits rows are staged in
+// LDS and read as float4 broadcasts, and the X loads of kDwUnroll tokens are
+// in flight before their FMAs.  Each channel sums its tokens in token order,
+// so the partials do not depend on CPT or the unrolling.  At d_model 1536,
+// M = 16 the router backward measured 1.07 ms with one channel per thread and
+// one token at a time, 0.61 ms with two channels and 16 tokens ahead (four
+// channels: 0.69 ms, fewer workgroups in flight).
+template <int MB>
+constexpr int dw_cpt() { return MB <= 2 ? 2 : 1; }
+
 template <int MB>
 __global__ __launch_bounds__(kChan) void router_dw_partial_kernel(const float* __restrict__ dl,
                                                                  const uint16_t* __restrict__ X, int64_t N, int dm,
                                                                  int M, float* __restrict__ part,
                                                                  float* __restrict__ dbp) {
+  constexpr int CPT = dw_cpt<MB>();
   __shared__ float dls[kDwStage * MB * 16];
-  const int c = blockIdx.y * kChan + threadIdx.x;
+  const int c0 = (blockIdx.y * kChan + threadIdx.x) * CPT;  // dm is a multiple of 32: CPT channels all in or out
   const int64_t n0 = (int64_t)blockIdx.x * kDwTokens;
-  float acc[MB * 16];
+  float acc[MB * 16][CPT];
 #pragma unroll
-  for (int jj = 0; jj < MB * 16; ++jj) acc[jj] = 0.f;
+  for (int jj = 0; jj < MB * 16; ++jj)
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) acc[jj][k] = 0.f;
   float bacc = 0.f;  // threads jj < M of the first channel slice: db
   for (int s0 = 0; s0 < kDwTokens; s0 += kDwStage) {
     __syncthreads();
@@ -123,24 +138,52 @@ __global__ __launch_bounds__(kChan) void router_dw_partial_kernel(const float* _
     __syncthreads();
     if (blockIdx.y == 0 && threadIdx.x < M)
       for (int t = 0; t < kDwStage; ++t) bacc += dls[t * MB * 16 + threadIdx.x];
-    if (c < dm) {
-      for (int t = 0; t < kDwStage && n0 + s0 + t < N; ++t) {
-        const float x = __uint_as_float((uint32_t)X[(n0 + s0 + t) * dm + c] << 16);
+    if (c0 < dm) {
+      // kDwUnroll tokens' X loads in flight at once (rows past N read row N-1
+      // and meet zero dlogits, so they add nothing)
+      for (int t0 = 0; t0 < kDwStage; t0 += kDwUnroll) {
+        float x[kDwUnroll][CPT];
 #pragma unroll
-        for (int jj = 0; jj < MB * 16; jj += 4) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(&dls[t * MB * 16 + jj]);
-          acc[jj] = fmaf(v[0], x, acc[jj]);
-          acc[jj + 1] = fmaf(v[1], x, acc[jj + 1]);
-          acc[jj + 2] = fmaf(v[2], x, acc[jj + 2]);
-          acc[jj + 3] = fmaf(v[3], x, acc[jj + 3]);
+        for (int u = 0; u < kDwUnroll; ++u) {
+          int64_t n = n0 + s0 + t0 + u;
+          n = n < N ? n : N - 1;
+          const uint16_t* xp = X + n * dm + c0;
+          if constexpr (CPT == 4) {
+            const u32x2 v = *reinterpret_cast<const u32x2*>(xp);
+            x[u][0] = bf16_lo(v[0]); x[u][1] = bf16_hi(v[0]); x[u][2] = bf16_lo(v[1]); x[u][3] = bf16_hi(v[1]);
+          } else if constexpr (CPT == 2) {
+            const uint32_t v = *reinterpret_cast<const uint32_t*>(xp);
+            x[u][0] = bf16_lo(v); x[u][1] = bf16_hi(v);
+          } else {
+            x[u][0] = __uint_as_float((uint32_t)xp[0] << 16);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kDwUnroll; ++u) {
+          const int t = t0 + u;
+#pragma unroll
+          for (int jj = 0; jj < MB * 16; jj += 4) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(&dls[t * MB * 16 + jj]);
+#pragma unroll
+            for (int k = 0; k < CPT; ++k) {
+              acc[jj][k] = fmaf(v[0], x[u][k], acc[jj][k]);
+              acc[jj + 1][k] = fmaf(v[1], x[u][k], acc[jj + 1][k]);
+              acc[jj + 2][k] = fmaf(v[2], x[u][k], acc[jj + 2][k]);
+              acc[jj + 3][k] = fmaf(v[3], x[u][k], acc[jj + 3][k]);
+            }
+          }
         }
       }
     }
   }
-  if (c < dm) {
+  if (c0 < dm) {
 #pragma unroll
     for (int jj = 0; jj < MB * 16; ++jj)
-      if (jj < M) part[((int64_t)blockIdx.x * M + jj) * dm + c] = acc[jj];
+      if (jj < M) {
+        float* out = part + ((int64_t)blockIdx.x * M + jj) * dm + c0;
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) out[k] = acc[jj][k];
+      }
   }
   if (blockIdx.y == 0 && threadIdx.x < M) dbp[(int64_t)blockIdx.x * M + threadIdx.x] = bacc;
 }
@@ -167,7 +210,8 @@ void launch_router_bwd(const float* dl, const uint16_t* X, const uint16_t* Wr, i
                        float* dWr, float* db, float* part, float* dbp, int nblk, hipStream_t st) {
   const unsigned cblk = (unsigned)ceil_div(dm, kChan);
   router_dx_kernel<MB><<<dim3((unsigned)ceil_div(N, kDxTokens), cblk), kChan, 0, st>>>(dl, Wr, N, dm, M, dX);
-  router_dw_partial_kernel<MB><<<dim3((unsigned)nblk, cblk), kChan, 0, st>>>(dl, X, N, dm, M, part, dbp);
+  const unsigned wblk = (unsigned)ceil_div(dm, kChan * dw_cpt<MB>());
+  router_dw_partial_kernel<MB><<<dim3((unsigned)nblk, wblk), kChan, 0, st>>>(dl, X, N, dm, M, part, dbp);
   router_dw_reduce_kernel<<<(unsigned)ceil_div((int64_t)M * dm, kChan), kChan, 0, st>>>(part, dbp, nblk, dm, M, dWr,
                                                                                        db);
 }
