@@ -194,8 +194,17 @@ __global__ __launch_bounds__(kChan) void router_dw_reduce_kernel(const float* __
                                                                 float* __restrict__ dWr, float* __restrict__ db) {
   const int64_t i = (int64_t)blockIdx.x * kChan + threadIdx.x;  // j * dm + c
   if (i < (int64_t)M * dm) {
+    // block order, as before; the unrolling only keeps 8 loads in flight
     float s = 0.f;
-    for (int b = 0; b < nblk; ++b) s += part[(int64_t)b * M * dm + i];
+    int b = 0;
+    for (; b + 8 <= nblk; b += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(b + u) * M * dm + i];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; b < nblk; ++b) s += part[(int64_t)b * M * dm + i];
     dWr[i] = s;
   }
   if (db && blockIdx.x == 0 && threadIdx.x < M) {
