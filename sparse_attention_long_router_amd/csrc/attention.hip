@@ -13,17 +13,21 @@
 // hardware interleaves one wave's softmax with the other's MFMAs; QB = 2:
 // 4 waves, one per SIMD, each K/V operand read feeding two MFMAs).  Per
 // 64-key tile:
-//   K and V rows arrive in LDS by 16-byte direct-to-LDS loads, double
-//   buffered (the next tile streams in while this one computes) and
-//   XOR-swizzled at 16-byte granularity (conflict-free reads);
+//   K and V rows arrive in LDS by 16-byte direct-to-LDS loads, XOR-swizzled
+//   at 16-byte granularity (conflict-free reads), into four buffers with one
+//   barrier per two tiles (the next pair streams in while this one computes;
+//   index-map windows, whose key-row table needs the LDS, keep two buffers
+//   and one barrier per tile); a tile's loads are issued after the first K
+//   operand reads of the tile before it;
 //   S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = the
 //   wave's Q fragment held in registers) -- the C layout gives every lane one
 //   query and 16 keys, so softmax statistics stay in-lane (the two wave
 //   halves share a query and exchange one value with v_permlane32_swap);
-//   softmax in float32 with exp2 and the scale folded into one FMA, against
-//   an exponent offset fixed from each row's first 32 keys (no accumulator
-//   rescaling; a work item where a row's sum of weights against that offset
-//   reaches 2^64 or overflows is recomputed with exact row maxima);
+//   softmax in float32 with exp2: the Q fragments carry the softmax scale in
+//   log2 units, and the exponent offset is fixed before the key loop (none
+//   at all when every row's first 32 scores are moderate, else their max),
+//   so there is no accumulator rescaling; a work item whose denominator or
+//   accumulator leaves the safe range is recomputed exactly;
 //   O^T += V^T P^T with the same MFMA: B = P^T comes straight from the S^T
 //   registers (the k-slot order of an MFMA is free as long as both operands
 //   agree), A = V^T comes from row-major V in LDS through two
@@ -37,7 +41,6 @@
 #ifndef MOGA_ATTN_QB
 #define MOGA_ATTN_QB 1
 #endif
-
 #include "moga_internal.h"
 
 // LLVM's raw buffer load to LDS (buffer_load_dwordx4 ... lds): descriptor,
@@ -264,6 +267,8 @@ struct RowState {
   float l;      // this lane's share of the denominator
 };
 constexpr float kLimit = 18446744073709551616.0f;  // 2^64
+constexpr float kTiny = 5.42101086242752217e-20f;     // 2^-64
+constexpr float kFastLo = -64.f, kFastHi = 32.f;     // offset-free range of the first scores (log2 units)
 
 // max / sum of a value over the two wave halves (lanes c and c+32 share a query)
 __device__ __forceinline__ float halves_max(float v) {
@@ -426,31 +431,44 @@ __device__ __forceinline__ void issue_tile_idx(const uint16_t* __restrict__ K, c
   }
 }
 
+// How a score becomes an exponent: kExpFree: s' (the Q fragments carry the
+// softmax scale in log2 units, no offset); kExpSub: s' - m_ref (scaled Q,
+// offset); kExpFma: s * scale_log2 - m_ref (unscaled Q: the training forward).
+enum { kExpFree = 0, kExpSub = 1, kExpFma = 2 };
+
 // Softmax step of one query block over one 32-key half of a tile: bf16 P^T
 // operands of the half's two 16-key MFMA steps go to pb, their sum to st.l.
 // s: reg r is key 8*(r/4) + 4*hh + r%4 of the half (masked keys are -inf).
+template <int kExp>
 __device__ __forceinline__ void softmax_half(const f32x16& s, RowState& st, float scale_log2, bf16x8 (&pb)[2]) {
-  float rs = 0.f;
+  float rs = st.l;
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(s[8 * t + j], scale_log2, -st.m_ref));
+      float x = s[8 * t + j];
+      if constexpr (kExp == kExpSub) x -= st.m_ref;
+      if constexpr (kExp == kExpFma) x = fmaf(x, scale_log2, -st.m_ref);
+      const float p = __builtin_amdgcn_exp2f(x);
       pb[t][j] = (__bf16)p;
       rs += p;
     }
-  st.l += rs;
+  st.l = rs;
 }
 
 // S^T of one 32-key half kb for the wave's QB query blocks; each K operand
 // read from LDS feeds QB MFMAs.  Reg r of s[b] is key kb*32 + 8*(r/4) + 4*hh + r%4.
-template <int D, int QB>
+struct NoOp {
+  __device__ __forceinline__ void operator()() const {}
+};
+template <int D, int QB, class AfterLoads = NoOp>
 __device__ __forceinline__ void qk_half(const uint16_t* Ks, const bf16x8 (&qf)[QB][D / 16], int kb, int lane,
-                                        f32x16 (&s)[QB]) {
+                                        f32x16 (&s)[QB], AfterLoads after_loads = {}) {
   constexpr int CPR = D / 8;
   const int hh = lane >> 5, krow = kb * 32 + (lane & 31);
 #pragma unroll
   for (int b = 0; b < QB; ++b) s[b] = f32x16{};
+
   // All K operands of the half first, then the dependent MFMA chain: without
   // the fence the scheduler reuses one operand register and exposes an LDS
   // round trip before every MFMA of the chain.
@@ -458,6 +476,7 @@ __device__ __forceinline__ void qk_half(const uint16_t* Ks, const bf16x8 (&qf)[Q
 #pragma unroll
   for (int st = 0; st < D / 16; ++st)
     ka[st] = *reinterpret_cast<const bf16x8*>(Ks + krow * D + ((2 * st + hh) ^ kswz(krow, CPR)) * 8);
+  after_loads();
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int st = 0; st < D / 16; ++st) {
@@ -530,35 +549,42 @@ __device__ __forceinline__ void mask_half(f32x16 (&s)[QB], int key0, int len, in
 
 // One 64-key tile for the wave's query blocks, in 32-key halves:
 //   QK(h0) QK(h1) | softmax(h0) PV(h0) | softmax(h1) PV(h1)
-template <int D, int QB, bool kMask, bool kVt>
+template <int D, int QB, bool kMask, bool kVt, int kExp, class AfterLoads = NoOp>
 __device__ __forceinline__ void tile_step(const uint16_t* Ks, const uint16_t* Vs, int k0, int len,
                                           const bf16x8 (&qf)[QB][D / 16], f32x16 (&o)[QB][D / 32],
-                                          RowState (&rs)[QB], float scale_log2, int lane) {
+                                          RowState (&rs)[QB], float scale_log2, int lane,
+                                          AfterLoads after_loads = {}) {
   const int hh = lane >> 5;
   f32x16 s0[QB], s1[QB];
   bf16x8 p[QB][2];
-  qk_half<D, QB>(Ks, qf, 0, lane, s0);
+  __builtin_amdgcn_s_setprio(1);
+  // The score chains issue at raised wave priority: when both waves of a SIMD
+  // have an instruction ready, the one with MFMAs to issue goes first.
+  qk_half<D, QB>(Ks, qf, 0, lane, s0, after_loads);
   qk_half<D, QB>(Ks, qf, 1, lane, s1);
+  __builtin_amdgcn_s_setprio(0);
   mask_half<kMask, QB, kVt>(s0, k0, len, hh);
 #pragma unroll
-  for (int b = 0; b < QB; ++b) softmax_half(s0[b], rs[b], scale_log2, p[b]);
+  for (int b = 0; b < QB; ++b) softmax_half<kExp>(s0[b], rs[b], scale_log2, p[b]);
   if constexpr (kVt)
     pv_half_t<D, QB>(Vs, p, 0, lane, o);
   else
     pv_half<D, QB>(Vs, p, 0, lane, o);
   mask_half<kMask, QB, kVt>(s1, k0 + 32, len, hh);
 #pragma unroll
-  for (int b = 0; b < QB; ++b) softmax_half(s1[b], rs[b], scale_log2, p[b]);
+  for (int b = 0; b < QB; ++b) softmax_half<kExp>(s1[b], rs[b], scale_log2, p[b]);
   if constexpr (kVt)
     pv_half_t<D, QB>(Vs, p, 1, lane, o);
   else
     pv_half<D, QB>(Vs, p, 1, lane, o);
 }
 
-// Row maxima only (the first pass of the exact recomputation).
+// Row maxima and sums (the first pass of the exact recomputation): per lane
+// half, the running max mx and the sum l of 2^(s' - mx), rescaled when the
+// max grows.  sc converts an MFMA score to log2 units.
 template <int D, int QB, bool kMask, bool kVt>
-__device__ __forceinline__ void tile_max(const uint16_t* Ks, int k0, int len, const bf16x8 (&qf)[QB][D / 16],
-                                         float (&mx)[QB], int lane) {
+__device__ __forceinline__ void tile_stats(const uint16_t* Ks, int k0, int len, const bf16x8 (&qf)[QB][D / 16],
+                                           float sc, float (&mx)[QB], float (&l)[QB], int lane) {
   const int hh = lane >> 5;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
@@ -566,9 +592,17 @@ __device__ __forceinline__ void tile_max(const uint16_t* Ks, int k0, int len, co
     qk_half<D, QB>(Ks, qf, kb, lane, s);
     mask_half<kMask, QB, kVt>(s, k0 + 32 * kb, len, hh);
 #pragma unroll
-    for (int b = 0; b < QB; ++b)
+    for (int b = 0; b < QB; ++b) {
+      float m = mx[b];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx[b] = fmaxf(mx[b], s[b][r]);
+      for (int r = 0; r < 16; ++r) m = fmaxf(m, s[b][r] * sc);
+      const float ms = m == -INFINITY ? 0.f : m;  // a lane half with every key so far masked
+      float add = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) add += __builtin_amdgcn_exp2f(s[b][r] * sc - ms);
+      l[b] = l[b] * __builtin_amdgcn_exp2f(mx[b] - ms) + add;
+      mx[b] = m;
+    }
   }
 }
 
@@ -597,15 +631,31 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave) void attn_kernel(
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
   constexpr int NW = waves_for<QB>();
-  __shared__ __attribute__((aligned(1024))) uint16_t Ks0[kBN * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t Vs0[kBN * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t Ks1[kBN * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t Vs1[kBN * D];
+  // The Q fragments carry the softmax scale in log2 units, except in the
+  // training forward: its saved log-sum-exp is paired with the unscaled Q by
+  // the backward pass.
+  constexpr bool kPre = kEpi != kEpiPlainLse;
+  // Four K/V buffers and one barrier per two tiles (the index-map windows
+  // keep two: their key-row table needs the LDS).  K buffers first, so that
+  // every K read (and every V read) is one base address plus an offset below
+  // 64 KB.
+  constexpr bool kPair = !Rows::kTable;
+  constexpr int NBUF = kPair ? 4 : 2;
+  __shared__ __attribute__((aligned(1024))) uint16_t kv_lds[2 * NBUF][kBN * D];
+  uint16_t* const Ks0 = kv_lds[0];
+  uint16_t* const Ks1 = kv_lds[1];
+  uint16_t* const Vs0 = kv_lds[NBUF];
+  uint16_t* const Vs1 = kv_lds[NBUF + 1];
+  [[maybe_unused]] uint16_t* const Ks2 = kv_lds[kPair ? 2 : 0];
+  [[maybe_unused]] uint16_t* const Ks3 = kv_lds[kPair ? 3 : 0];
+  [[maybe_unused]] uint16_t* const Vs2 = kv_lds[kPair ? NBUF + 2 : 0];
+  [[maybe_unused]] uint16_t* const Vs3 = kv_lds[kPair ? NBUF + 3 : 0];
 
   Work w;
   if (!rows.decode(xcd_remap(blockIdx.x, kXcdRun), w)) return;  // uniform per block
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave: scalar address arithmetic
   const int hh = lane >> 5, c = lane & 31;
   const int64_t hoff = (int64_t)w.head * D;
   const int nfull = w.len / kBN;            // tiles without a group end inside
@@ -646,8 +696,14 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave) void attn_kernel(
       issue_tile<D, NW>(K, V, Kd, Vd, rows, w, row_stride, hoff, t * kBN, wave, lane);
     }
   };
-  if constexpr (Rows::kIndirect) fetch_keys<D, NW>(rows, w, 0, wave, lane, kidx);
-  issue(Ks0, Vs0, 0);
+  auto issue_first = [&]() {
+    if constexpr (Rows::kIndirect) fetch_keys<D, NW>(rows, w, 0, wave, lane, kidx);
+    issue(Ks0, Vs0, 0);
+    if constexpr (kPair) {
+      if (1 < ntiles) issue(Ks1, Vs1, 1);
+    }
+  };
+  issue_first();
 
   // this lane's two queries (blocks b = 0, 1) and their Q fragments
   int64_t qrow[QB];
@@ -660,8 +716,15 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave) void attn_kernel(
     qrow[b] = rows.row(w, qvalid[b] ? qi : w.nq - 1);
     const uint16_t* qp = Q + qrow[b] * row_stride + hoff + 8 * hh;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qf[b][s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
+    for (int s = 0; s < KSTEPS; ++s) {
+      qf[b][s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
+      if constexpr (kPre) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) qf[b][s][j] = (__bf16)((float)qf[b][s][j] * scale_log2);
+      }
+    }
   }
+  const float sc = kPre ? 1.f : scale_log2;  // log2 units per unit of an MFMA score
 
   // A wave whose queries all lie past the group end (the last query tile of a
   // group) computes nothing, freeing its SIMD for the wave that shares it.
@@ -676,91 +739,186 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave) void attn_kernel(
     rs[b] = {0.f, 0.f};
   }
 
-  // Tile t lives in buffer t % 2.  At the top of each tile: wait for this
-  // wave's loads, barrier (all waves' loads landed, tile t-1 fully consumed),
-  // then start the loads of tile t+1 into the other buffer.
+  // Two buffers (index-map windows): tile t lives in buffer t % 2.  At the
+  // top of each tile: wait for this wave's loads, barrier (all waves' loads
+  // landed, tile t-1 fully consumed); the tile's step then starts the loads
+  // of tile t+1 into the other buffer once its first K operand reads are
+  // issued.
   auto begin_tile = [&](uint16_t* Kn, uint16_t* Vn, int t) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 1 < ntiles) issue(Kn, Vn, t + 1);
   };
-  // kMax: row maxima only (into mx) instead of softmax and P V
-  auto run = [&](auto max_only) {
-    constexpr bool kMax = decltype(max_only)::value;
-    float mx[QB];
+  // One pass over the keys: kExpFree / kExpSub / kExpFma (softmax and P V),
+  // or kStats (row maxima and sums into mx, lsum).
+  constexpr int kStats = 3;
+  float mx[QB], lsum[QB];
+  auto run = [&](auto mode) {
+    constexpr int kMode = decltype(mode)::value;
 #pragma unroll
-    for (int b = 0; b < QB; ++b) mx[b] = -INFINITY;
-    auto step = [&](const uint16_t* Ks, const uint16_t* Vs, int t, auto mask) {
+    for (int b = 0; b < QB; ++b) {
+      mx[b] = -INFINITY;
+      lsum[b] = 0.f;
+    }
+    // one tile; dma() loads later tiles after this tile's first K operand reads
+    auto step = [&](uint16_t* Ks, uint16_t* Vs, int t, auto mask, uint16_t* Kn, uint16_t* Vn) {
       constexpr bool kMask = decltype(mask)::value;
-      if (!wave_live) return;  // keeps its barriers and loads, skips the math
-      if constexpr (kMax)
-        tile_max<D, QB, kMask, Rows::kVt>(Ks, t * kBN, w.len, qf, mx, lane);
-      else
-        tile_step<D, QB, kMask, Rows::kVt>(Ks, Vs, t * kBN, w.len, qf, o, rs, scale_log2, lane);
+      auto dma = [&]() {
+        if (t + 1 < ntiles) issue(Kn, Vn, t + 1);
+      };
+      if (!wave_live) {  // keeps its barriers and loads, skips the math
+        dma();
+        return;
+      }
+      if constexpr (kMode == kStats) {
+        dma();
+        tile_stats<D, QB, kMask, Rows::kVt>(Ks, t * kBN, w.len, qf, sc, mx, lsum, lane);
+      } else {
+        tile_step<D, QB, kMask, Rows::kVt, kMode>(Ks, Vs, t * kBN, w.len, qf, o, rs, scale_log2, lane, dma);
+      }
     };
     using F = std::false_type;
     using T = std::true_type;
     int t = 0;
+    if constexpr (kPair) {
+      // tiles t, t+1 in buffers 0, 1 (t % 4 == 0) or 2, 3: at the top of
+      // each pair, wait for this wave's loads, barrier, and (after the
+      // pair's first K operand reads) load the next pair into the other two.
+      auto pair_dma = [&](uint16_t* Ka, uint16_t* Va, uint16_t* Kb2, uint16_t* Vb2, int t0) {
+        return [=, &issue]() {
+          if (t0 + 2 < ntiles) issue(Ka, Va, t0 + 2);
+          if (t0 + 3 < ntiles) issue(Kb2, Vb2, t0 + 3);
+        };
+      };
+      auto sync = [&]() {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      };
+      auto pstep = [&](uint16_t* Ks, uint16_t* Vs, int tt, auto mask, auto dma) {
+        constexpr bool kMask = decltype(mask)::value;
+        if (!wave_live) {
+          dma();
+          return;
+        }
+        if constexpr (kMode == kStats) {
+          dma();
+          tile_stats<D, QB, kMask, Rows::kVt>(Ks, tt * kBN, w.len, qf, sc, mx, lsum, lane);
+        } else {
+          tile_step<D, QB, kMask, Rows::kVt, kMode>(Ks, Vs, tt * kBN, w.len, qf, o, rs, scale_log2, lane, dma);
+        }
+      };
+      const NoOp none{};
+      for (; t + 4 <= nfull; t += 4) {
+        sync();
+        pstep(Ks0, Vs0, t, F{}, pair_dma(Ks2, Vs2, Ks3, Vs3, t));
+        pstep(Ks1, Vs1, t + 1, F{}, none);
+        sync();
+        pstep(Ks2, Vs2, t + 2, F{}, pair_dma(Ks0, Vs0, Ks1, Vs1, t + 2));
+        pstep(Ks3, Vs3, t + 3, F{}, none);
+      }
+      if (t < ntiles) {  // one to four tiles left, only the last may be partial; t % 4 == 0
+        sync();
+        if (t < nfull)
+          pstep(Ks0, Vs0, t, F{}, pair_dma(Ks2, Vs2, Ks3, Vs3, t));
+        else
+          pstep(Ks0, Vs0, t, T{}, pair_dma(Ks2, Vs2, Ks3, Vs3, t));
+        if (t + 1 < ntiles) {
+          if (t + 1 < nfull) pstep(Ks1, Vs1, t + 1, F{}, none); else pstep(Ks1, Vs1, t + 1, T{}, none);
+        }
+        if (t + 2 < ntiles) {
+          sync();
+          if (t + 2 < nfull)
+            pstep(Ks2, Vs2, t + 2, F{}, none);
+          else
+            pstep(Ks2, Vs2, t + 2, T{}, none);
+          if (t + 3 < ntiles) pstep(Ks3, Vs3, t + 3, T{}, none);
+        }
+      }
+      return;
+    }
     for (; t + 2 <= nfull; t += 2) {
       begin_tile(Ks1, Vs1, t);
-      step(Ks0, Vs0, t, F{});
+      step(Ks0, Vs0, t, F{}, Ks1, Vs1);
       begin_tile(Ks0, Vs0, t + 1);
-      step(Ks1, Vs1, t + 1, F{});
+      step(Ks1, Vs1, t + 1, F{}, Ks0, Vs0);
     }
     if (t < ntiles) {  // one or two tiles left, the last may be partial; t is even
       begin_tile(Ks1, Vs1, t);
       if (t < nfull)
-        step(Ks0, Vs0, t, F{});
+        step(Ks0, Vs0, t, F{}, Ks1, Vs1);
       else
-        step(Ks0, Vs0, t, T{});
+        step(Ks0, Vs0, t, T{}, Ks1, Vs1);
       if (t + 1 < ntiles) {
         begin_tile(Ks0, Vs0, t + 1);
-        step(Ks1, Vs1, t + 1, T{});
+        step(Ks1, Vs1, t + 1, T{}, Ks0, Vs0);
       }
     }
-    if constexpr (kMax) {
-#pragma unroll
-      for (int b = 0; b < QB; ++b) rs[b] = {halves_max(mx[b]) * scale_log2, 0.f};
-    }
   };
-  // Exponent offsets from each row's first 32 keys (key 0 always exists).
+  // Exponent offsets from each row's first 32 keys (key 0 always exists); a
+  // wave whose rows all have those scores in [kFastLo, kFastHi] runs with no
+  // offset at all.
   {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
+  bool free_ok = true;
   if (wave_live) {
     f32x16 s[QB];
     qk_half<D, QB>(Ks0, qf, 0, lane, s);
     if (w.len < 32) mask_half<true, QB, Rows::kVt>(s, 0, w.len, hh);
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
-      float mx = s[b][0];
+      float m = s[b][0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
-      rs[b].m_ref = halves_max(mx) * scale_log2;
+      for (int r = 1; r < 16; ++r) m = fmaxf(m, s[b][r]);
+      m = halves_max(m) * sc;
+      rs[b].m_ref = m;
+      free_ok &= m >= kFastLo && m <= kFastHi;
     }
   }
-  run(std::false_type{});
-
-  // Scores far above a row's first keys would overflow the fixed offset (the
-  // denominator is not finite or reaches kLimit): recompute this work item
-  // exactly (row maxima first, then softmax and P V with the exact maxima).
-  bool over = false;
+  if (kPre && __builtin_amdgcn_ballot_w64(!free_ok) == 0) {  // uniform per wave
 #pragma unroll
-  for (int b = 0; b < QB; ++b) over |= !(halves_sum(rs[b].l) < kLimit);
+    for (int b = 0; b < QB; ++b) rs[b].m_ref = 0.f;
+    run(std::integral_constant<int, kExpFree>{});
+  } else {
+    run(std::integral_constant<int, kPre ? kExpSub : kExpFma>{});
+  }
+
+  // A denominator outside [2^-64, 2^64) or a non-finite accumulator (scores
+  // far from the offset, or very large values) sends the work item to the
+  // exact recomputation: row maxima and sums first, then softmax and P V
+  // against max + log2(sum), which keeps every weight at most 1 and the
+  // accumulator within the magnitude of the values.
+  bool over = false;
+  if (wave_live) {
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      const float tot = halves_sum(rs[b].l);
+      over |= !(tot < kLimit) || !(tot >= kTiny);
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) over |= !(__builtin_fabsf(o[b][db][r]) <= 3.402823466e38f);
+    }
+  }
   if (__syncthreads_or(over)) {
     __syncthreads();
-    if constexpr (Rows::kIndirect) fetch_keys<D, NW>(rows, w, 0, wave, lane, kidx);
-    issue(Ks0, Vs0, 0);
-    run(std::true_type{});
-    __syncthreads();
-    if constexpr (Rows::kIndirect) fetch_keys<D, NW>(rows, w, 0, wave, lane, kidx);
-    issue(Ks0, Vs0, 0);
+    issue_first();
+    run(std::integral_constant<int, kStats>{});
 #pragma unroll
-    for (int b = 0; b < QB; ++b)
+    for (int b = 0; b < QB; ++b) {
+      const auto m2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx[b]), __float_as_uint(mx[b]), false, false);
+      const auto l2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum[b]), __float_as_uint(lsum[b]), false, false);
+      const float m0 = __uint_as_float(m2[0]), m1 = __uint_as_float(m2[1]);
+      const float mm = fmaxf(m0, m1);  // finite: key 0 lies in lane half 0
+      const float ll = __uint_as_float(l2[0]) * __builtin_amdgcn_exp2f(m0 - mm) +
+                       __uint_as_float(l2[1]) * __builtin_amdgcn_exp2f(m1 - mm);
+      rs[b] = {mm + __log2f(ll), 0.f};
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) o[b][db] = f32x16{};
-    run(std::false_type{});
+    }
+    __syncthreads();
+    issue_first();
+    run(std::integral_constant<int, kPre ? kExpSub : kExpFma>{});
   }
 
   // ---- normalise and store: reg r of block db is channel 32*db + 8*(r/4) + 4*hh + r%4

@@ -13,8 +13,10 @@ MEAN_ABS = 2e-3
 REL_FRO = 1e-2
 # float32 gate: its error is at most 2 max_j |dr_j| plus the exp error, where dr
 # is the float32 score error, about sqrt(d/32) 2^-24 |r| for MFMA partial sums
-# of 32 products (~1e-6 at d_model = 5120).
-GATE_RTOL = 1e-4
+# of 32 products: ~4e-6 for |r| ~ 5 at d_model = 5120, the widest router.  The
+# largest error measured over every full-size workload is 4.1e-6 (d_model
+# 5120), 2.6e-6 at d_model 1536.
+GATE_RTOL = 1e-5
 
 # Gradients (backward pass): bf16 operands P, dS and the gated upstream
 # gradient each carry a 2^-9 relative rounding, accumulated in float32, and
@@ -62,12 +64,16 @@ def assert_grad_close(got, want, what="grad"):
     return e
 
 
-def assert_gate_close(got, want):
+def assert_gate_close(got, want, what="gate"):
+    """Relative gate error against the oracle's float64 gate; the measured
+    maximum is printed (pytest -s shows it) and returned."""
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)
     rel = np.abs(got - want) / np.abs(want)
-    assert rel.max() <= GATE_RTOL, f"gate rel err {rel.max():.3g} > {GATE_RTOL}"
-    return float(rel.max())
+    worst = float(rel.max()) if rel.size else 0.0
+    print(f"[gate] {what}: max relative error {worst:.3g} over {rel.size} tokens (bar {GATE_RTOL})", flush=True)
+    assert worst <= GATE_RTOL, f"{what} rel err {worst:.3g} > {GATE_RTOL}"
+    return worst
 
 
 def bf16_round(a):

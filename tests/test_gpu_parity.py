@@ -440,9 +440,80 @@ def test_attention_score_growth(moga, late, label):
     assert torch.equal(pv["perm"].cpu(), torch.arange(N, dtype=torch.int32))
     Ot = moga.moga_group_attention_unpermute_vt(pv["Qp"], pv["Kp"], pv["Vt"], pv["cu_seqlens"], pv["perm"], gate)
     Oq = moga.moga_group_attention_unpermute_vtq(Qd, pv["Kp"], pv["Vt"], pv["cu_seqlens"], pv["perm"], gate)
+    # and the gather-on-load instantiation (keys fetched through perm), whose
+    # recomputation re-fetches the first tiles' key rows
+    Of = moga.moga_group_attention_fused(Qd, Kd, Vd, pv["cu_seqlens"], pv["perm"], gate)
     torch.cuda.synchronize()
     assert_output_close(_np(Ot), ref, f"O transposed V ({label})")
     assert torch.equal(Oq, Ot)
+    assert_output_close(_np(Of), ref, f"O gather on load ({label})")
+
+
+@pytest.mark.parametrize("path", ["group_attention", "vtq", "fused"])
+def test_attention_large_values(moga, path):
+    """Large but finite values with late score growth: |V| ~ 2^100 and scores
+    that climb to ~49 log2 units past the first keys, so the float32 sum of
+    weight x value overflows while the denominator (~2^58) stays below 2^64.
+    The result must still be the softmax average (exact up to rounding), which
+    is the plain-size result scaled by 2^100 (powers of two scale exactly)."""
+    print(f"[parity] large values {path}", flush=True)
+    N, H, D = 700, 2, 128
+    g = torch.Generator().manual_seed(11)
+    Q = torch.full((N, H, D), 2.0).bfloat16()
+    K = torch.zeros((N, H, D))
+    K[200:] = 1.5 + 0.25 * torch.randn((N - 200, H, D), generator=g)
+    K = K.bfloat16()
+    V = torch.randn((N, H, D), generator=g).bfloat16()
+    big = 2.0 ** 100
+    Vb = (V.float() * big).bfloat16()
+    assert torch.equal(Vb.float() / big, V.float())
+    cu = torch.tensor([0, 100, N], dtype=torch.int32)
+    ref = oracle.group_attention(_np(Q), _np(K), _np(V), cu.numpy(), 1 / math.sqrt(D))
+    Qd, Kd, Vd = Q.to(DEV), K.to(DEV), Vb.to(DEV)
+    if path == "group_attention":
+        out = moga.moga_group_attention(Qd, Kd, Vd, cu.to(DEV))
+    else:
+        gid = torch.cat([torch.zeros(100, dtype=torch.int32), torch.ones(N - 100, dtype=torch.int32)]).to(DEV)
+        gate = torch.ones(N, dtype=torch.float32, device=DEV)
+        pv = moga.moga_permute_vt(gid, 2, None, Kd, Vd)
+        if path == "vtq":
+            out = moga.moga_group_attention_unpermute_vtq(Qd, pv["Kp"], pv["Vt"], pv["cu_seqlens"], pv["perm"], gate)
+        else:
+            out = moga.moga_group_attention_fused(Qd, Kd, Vd, pv["cu_seqlens"], pv["perm"], gate)
+    torch.cuda.synchronize()
+    got = _np(out)
+    assert np.isfinite(got).all(), "large-value output is not finite"
+    assert_output_close(got / big, ref, f"large values ({path})")
+
+
+@pytest.mark.parametrize("late", [0.9, 2.0, 4.0])
+def test_stga_score_growth(moga, late):
+    """Static and shot-aware windows whose later frames' keys score far above
+    the first frame's (the exponent offset comes from a window's first 32
+    keys): the index-map instantiations must engage their exact recomputation
+    where needed and match the oracle."""
+    T, Hs, Ws, win_t, th, tw, H, D = 6, 6, 10, 3, 6, 10, 2, 128
+    N = T * Hs * Ws
+    print(f"[parity] stga score growth late={late}", flush=True)
+    g = torch.Generator().manual_seed(13)
+    Q = torch.full((N, H, D), 2.0).bfloat16()
+    K = torch.zeros((N, H, D))
+    frame = torch.arange(N) // (Hs * Ws)
+    lateK = (frame % win_t) > 0                     # every window's frames after its first
+    K[lateK] = late + 0.25 * torch.randn((int(lateK.sum()), H, D), generator=g)
+    K = K.bfloat16()
+    V = torch.randn((N, H, D), generator=g).bfloat16()
+    Qd, Kd, Vd = Q.to(DEV), K.to(DEV), V.to(DEV)
+    out = moga.moga_stga_attention(Qd, Kd, Vd, T, Hs, Ws, win_t, th, tw)
+    shots = [0, 3, 6]
+    outs = moga.moga_stga_shot_attention(Qd, Kd, Vd, T, Hs, Ws, torch.tensor(shots, dtype=torch.int32, device=DEV),
+                                         win_t, th, tw, augment=1)
+    torch.cuda.synchronize()
+    sc = 1 / math.sqrt(D)
+    ref = oracle.stga_attention(_np(Q), _np(K), _np(V), T, Hs, Ws, win_t, th, tw, sc)
+    refs = oracle.stga_shot_attention(_np(Q), _np(K), _np(V), T, Hs, Ws, shots, win_t, th, tw, sc, 1)
+    assert_output_close(_np(out), ref, f"STGA growth {late}")
+    assert_output_close(_np(outs), refs, f"shot STGA growth {late}")
 
 
 @pytest.mark.parametrize("name,M", [("tiny", 4), ("clip30s_122f", 16), ("minute_372f", 32)])
