@@ -73,11 +73,13 @@ typedef enum moga_op {
  *   bias     float [M] or NULL (no bias)
  *   group_id int32 [N]  (output)
  *   gate     float [N]  (output)
- *   Needs no workspace.
+ *   ws, ws_bytes  workspace of moga_workspace_bytes(MOGA_OP_ROUTE, ...) = 0
+ *            bytes: the route needs none, so ws may be NULL; the arguments
+ *            keep the signature of the other steps.
  */
 int moga_route(const void* X, const void* Wr, const float* bias,
                int64_t N, int32_t d_model, int32_t M,
-               int32_t* group_id, float* gate, void* stream);
+               int32_t* group_id, float* gate, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moga_permute -- make every group contiguous (Algorithm 1 step 2).
@@ -108,10 +110,15 @@ int moga_permute(const int32_t* group_id, const void* Q, const void* K, const vo
  *   softmax_scale  > 0, or <= 0 for 1/sqrt(D)
  *   Op          bf16 [N, H, D] (output, permuted order, no gate)
  *   ws          workspace of at least moga_workspace_bytes(MOGA_OP_GROUP_ATTENTION, N, M, H, D)
- *   bf16 MFMA products and float32 accumulation; the float32 softmax runs
- *   against a per-row exponent offset taken from the row's first 32 keys, and
- *   a work item whose later scores would overflow it is recomputed with its
- *   exact row maxima, so the result is the exact softmax for any finite input.
+ *   bf16 MFMA products and float32 accumulation.  The Q operand carries the
+ *   softmax scale (in log2 units, rounded to bf16 once per element) and the
+ *   float32 softmax runs against a per-row exponent offset fixed before the
+ *   key loop: none when the row's first 32 scores are moderate, else their
+ *   maximum.  A work item whose denominator leaves [2^-64, 2^64) or whose
+ *   float32 accumulator is not finite is recomputed against each row's exact
+ *   maximum plus log2 of its exact sum, so every weight is at most 1 and the
+ *   accumulator stays within the magnitude of the values: for any finite
+ *   input the result is the softmax average of the group's values.
  */
 int moga_group_attention(const void* Qp, const void* Kp, const void* Vp,
                          const int32_t* cu_seqlens, int64_t N, int32_t H, int32_t D,
@@ -221,12 +228,14 @@ int moga_unpermute(const void* Op, const int32_t* perm, const float* gate,
  *   O[n] = beta * O[n] + alpha * STGA(n)   (beta = 0: O is not read).
  *   Q, K, V bf16 [N, H, D]; O bf16 [N, H, D] (in/out).
  *   win_t, tile_h, tile_w must divide T, Hs, Ws; the group size
- *   win_t * tile_h * tile_w must be at most 2^20.  Needs no workspace.
+ *   win_t * tile_h * tile_w must be at most 2^20.
+ *   ws, ws_bytes  workspace of moga_workspace_bytes(MOGA_OP_STGA_ATTENTION, ...)
+ *   = 0 bytes: the static windows need none, so ws may be NULL.
  */
 int moga_stga_attention(const void* Q, const void* K, const void* V,
                         int32_t T, int32_t Hs, int32_t Ws, int32_t win_t, int32_t tile_h,
                         int32_t tile_w, int32_t H, int32_t D, float softmax_scale,
-                        float alpha, float beta, void* O, void* stream);
+                        float alpha, float beta, void* O, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moga_stga_shot_attention -- the shot-aware STGA branch (section "Spatial-

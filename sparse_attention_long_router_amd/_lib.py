@@ -28,7 +28,7 @@ MOGA_OP_ATTENTION_BACKWARD = 7
 _c = ctypes
 _vp, _i32, _i64, _f32, _sz = _c.c_void_p, _c.c_int32, _c.c_int64, _c.c_float, _c.c_size_t
 SIGNATURES = {
-    "moga_route": (_c.c_int, [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp]),
+    "moga_route": (_c.c_int, [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "moga_permute": (_c.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _sz, _vp]),
     "moga_group_attention": (_c.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _f32, _vp, _vp, _sz, _vp]),
@@ -44,7 +44,7 @@ SIGNATURES = {
                                               _vp, _vp, _sz, _vp]),
     "moga_unpermute": (_c.c_int, [_vp, _vp, _vp, _i64, _i32, _i32, _f32, _vp, _vp]),
     "moga_stga_attention": (_c.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
-                                       _f32, _f32, _vp, _vp]),
+                                       _f32, _f32, _vp, _vp, _sz, _vp]),
     "moga_stga_shot_attention": (_c.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                                             _i32, _i32, _f32, _f32, _f32, _vp, _vp, _sz, _vp]),
     "moga_stga_shot_workspace_bytes": (_sz, [_i32, _i32, _i32]),
@@ -63,7 +63,7 @@ SIGNATURES = {
 
 BUILD_HINT = "run `python sparse_attention_long_router_amd/build.py`"
 # moga_version() of the sources this binding matches (csrc/api.hip)
-EXPECTED_VERSION = 301
+EXPECTED_VERSION = 400
 
 
 def _load():

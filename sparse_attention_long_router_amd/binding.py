@@ -57,7 +57,8 @@ def moga_route(X, Wr, bias=None, group_id=None, gate=None):
     gate = torch.empty(N, dtype=torch.float32, device=X.device) if gate is None else gate
     _need(group_id, "group_id", torch.int32, 1, (N,))
     _need(gate, "gate", torch.float32, 1, (N,))
-    check(_lib.LIB.moga_route(ptr(X), ptr(Wr), ptr(bias), N, d, M, ptr(group_id), ptr(gate), stream_handle()),
+    check(_lib.LIB.moga_route(ptr(X), ptr(Wr), ptr(bias), N, d, M, ptr(group_id), ptr(gate), None, 0,
+                              stream_handle()),
           "moga_route")
     return group_id, gate
 
@@ -289,7 +290,8 @@ def moga_stga_attention(Q, K, V, T, Hs, Ws, win_t, tile_h, tile_w, softmax_scale
     if T * Hs * Ws != N:
         raise ValueError("T*Hs*Ws must equal N")
     check(_lib.LIB.moga_stga_attention(ptr(Q), ptr(K), ptr(V), T, Hs, Ws, win_t, tile_h, tile_w, H, D,
-                                       float(softmax_scale), float(alpha), float(beta), ptr(O), stream_handle()),
+                                       float(softmax_scale), float(alpha), float(beta), ptr(O), None, 0,
+                                       stream_handle()),
           "moga_stga_attention")
     return O
 

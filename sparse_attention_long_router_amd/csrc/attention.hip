@@ -1085,8 +1085,11 @@ extern "C" int moga_group_attention(const void* Qp, const void* Kp, const void* 
 
 extern "C" int moga_stga_attention(const void* Q, const void* K, const void* V, int32_t T, int32_t Hs, int32_t Ws,
                                    int32_t win_t, int32_t tile_h, int32_t tile_w, int32_t H, int32_t D,
-                                   float softmax_scale, float alpha, float beta, void* O, void* stream) {
+                                   float softmax_scale, float alpha, float beta, void* O, void* ws,
+                                   size_t ws_bytes, void* stream) {
   using namespace moga;
+  (void)ws;  // static windows need no workspace (moga_workspace_bytes(MOGA_OP_STGA_ATTENTION, ...) == 0)
+  (void)ws_bytes;
   if (!Q || !K || !V || !O) return MOGA_ERR_NULL;
   if (T < 1 || Hs < 1 || Ws < 1 || win_t < 1 || tile_h < 1 || tile_w < 1 || H < 1 || D < 1) return MOGA_ERR_SHAPE;
   if (T % win_t || Hs % tile_h || Ws % tile_w) return MOGA_ERR_SHAPE;

@@ -253,8 +253,10 @@ void launch_route(const uint16_t* X, const uint16_t* Wr, const float* bias, int6
 }  // namespace moga
 
 extern "C" int moga_route(const void* X, const void* Wr, const float* bias, int64_t N, int32_t d_model,
-                          int32_t M, int32_t* group_id, float* gate, void* stream) {
+                          int32_t M, int32_t* group_id, float* gate, void* ws, size_t ws_bytes, void* stream) {
   using namespace moga;
+  (void)ws;  // the route needs no workspace (moga_workspace_bytes(MOGA_OP_ROUTE, ...) == 0)
+  (void)ws_bytes;
   if (!X || !Wr || !group_id || !gate) return MOGA_ERR_NULL;
   if (N < 1 || N >= (int64_t(1) << 31) || M < 1 || d_model < 1) return MOGA_ERR_SHAPE;
   if (M > kMaxGroups || d_model % 32 != 0) return MOGA_ERR_UNSUPPORTED;

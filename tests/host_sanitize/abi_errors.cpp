@@ -26,9 +26,9 @@ int main() {
   const size_t big = size_t(1) << 40;  // "enough" workspace
   const int64_t N = 1000;
 
-  expect(moga_route(nullptr, P, nullptr, N, 64, 4, I, F, nullptr), MOGA_ERR_NULL, "route X");
-  expect(moga_route(P, P, nullptr, 0, 64, 4, I, F, nullptr), MOGA_ERR_SHAPE, "route N");
-  expect(moga_route(P, P, nullptr, N, 64, 65, I, F, nullptr), MOGA_ERR_UNSUPPORTED, "route M");
+  expect(moga_route(nullptr, P, nullptr, N, 64, 4, I, F, nullptr, 0, nullptr), MOGA_ERR_NULL, "route X");
+  expect(moga_route(P, P, nullptr, 0, 64, 4, I, F, nullptr, 0, nullptr), MOGA_ERR_SHAPE, "route N");
+  expect(moga_route(P, P, nullptr, N, 64, 65, I, F, nullptr, 0, nullptr), MOGA_ERR_UNSUPPORTED, "route M");
 
   expect(moga_permute(nullptr, P, P, P, N, 2, 128, 4, P, P, P, I, I, I, P, big, nullptr), MOGA_ERR_NULL,
          "permute group_id");
@@ -60,9 +60,9 @@ int main() {
          MOGA_ERR_UNSUPPORTED, "attention_fused D");
 
   expect(moga_unpermute(P, I, nullptr, N, 2, 128, 0.f, P, nullptr), MOGA_ERR_NULL, "unpermute gate");
-  expect(moga_stga_attention(P, P, P, 5, 30, 52, 3, 30, 26, 2, 128, 0.f, 1.f, 0.f, P, nullptr), MOGA_ERR_SHAPE,
+  expect(moga_stga_attention(P, P, P, 5, 30, 52, 3, 30, 26, 2, 128, 0.f, 1.f, 0.f, P, nullptr, 0, nullptr), MOGA_ERR_SHAPE,
          "stga win_t does not divide T");
-  expect(moga_stga_attention(P, P, P, 6, 30, 52, 3, 30, 26, 2, 128, 0.f, 1.f, 0.f, nullptr, nullptr),
+  expect(moga_stga_attention(P, P, P, 6, 30, 52, 3, 30, 26, 2, 128, 0.f, 1.f, 0.f, nullptr, nullptr, 0, nullptr),
          MOGA_ERR_NULL, "stga O");
   expect(moga_stga_shot_attention(P, P, P, 6, 30, 52, I, 0, 3, 30, 26, 1, 2, 128, 0.f, 1.f, 0.f, P, P, big,
                                   nullptr),

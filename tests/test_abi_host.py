@@ -70,13 +70,13 @@ def test_workspace_sizes(lib):
 
 def test_route_argument_errors(lib):
     r = lib.moga_route
-    assert r(None, FAKE, None, 10, 64, 4, FAKE, FAKE, None) == ENULL
-    assert r(FAKE, FAKE, None, 10, 64, 4, None, FAKE, None) == ENULL
-    assert r(FAKE, FAKE, None, 0, 64, 4, FAKE, FAKE, None) == ESHAPE
-    assert r(FAKE, FAKE, None, 1 << 31, 64, 4, FAKE, FAKE, None) == ESHAPE
-    assert r(FAKE, FAKE, None, 10, 64, 0, FAKE, FAKE, None) == ESHAPE
-    assert r(FAKE, FAKE, None, 10, 64, 65, FAKE, FAKE, None) == EUNSUP
-    assert r(FAKE, FAKE, None, 10, 48, 4, FAKE, FAKE, None) == EUNSUP
+    assert r(None, FAKE, None, 10, 64, 4, FAKE, FAKE, None, 0, None) == ENULL
+    assert r(FAKE, FAKE, None, 10, 64, 4, None, FAKE, None, 0, None) == ENULL
+    assert r(FAKE, FAKE, None, 0, 64, 4, FAKE, FAKE, None, 0, None) == ESHAPE
+    assert r(FAKE, FAKE, None, 1 << 31, 64, 4, FAKE, FAKE, None, 0, None) == ESHAPE
+    assert r(FAKE, FAKE, None, 10, 64, 0, FAKE, FAKE, None, 0, None) == ESHAPE
+    assert r(FAKE, FAKE, None, 10, 64, 65, FAKE, FAKE, None, 0, None) == EUNSUP
+    assert r(FAKE, FAKE, None, 10, 48, 4, FAKE, FAKE, None, 0, None) == EUNSUP
 
 
 def test_permute_argument_errors(lib):
@@ -204,13 +204,13 @@ def test_unpermute_argument_errors(lib):
 
 def test_stga_argument_errors(lib):
     s = lib.moga_stga_attention
-    assert s(None, FAKE, FAKE, 6, 30, 52, 3, 30, 26, 2, 128, 0.0, 1.0, 0.0, FAKE, None) == ENULL
-    assert s(FAKE, FAKE, FAKE, 6, 30, 52, 4, 30, 26, 2, 128, 0.0, 1.0, 0.0, FAKE, None) == ESHAPE  # 4 !| 6
-    assert s(FAKE, FAKE, FAKE, 6, 30, 52, 3, 7, 26, 2, 128, 0.0, 1.0, 0.0, FAKE, None) == ESHAPE   # 7 !| 30
-    assert s(FAKE, FAKE, FAKE, 6, 30, 52, 3, 30, 25, 2, 128, 0.0, 1.0, 0.0, FAKE, None) == ESHAPE  # 25 !| 52
-    assert s(FAKE, FAKE, FAKE, 0, 30, 52, 1, 30, 26, 2, 128, 0.0, 1.0, 0.0, FAKE, None) == ESHAPE
-    assert s(FAKE, FAKE, FAKE, 6, 30, 52, 3, 30, 26, 2, 100, 0.0, 1.0, 0.0, FAKE, None) == EUNSUP
-    assert s(FAKE, FAKE, FAKE, 2048, 1024, 1024, 2048, 1024, 1024, 1, 64, 0.0, 1.0, 0.0, FAKE, None) == ESHAPE
+    assert s(None, FAKE, FAKE, 6, 30, 52, 3, 30, 26, 2, 128, 0.0, 1.0, 0.0, FAKE, None, 0, None) == ENULL
+    assert s(FAKE, FAKE, FAKE, 6, 30, 52, 4, 30, 26, 2, 128, 0.0, 1.0, 0.0, FAKE, None, 0, None) == ESHAPE  # 4 !| 6
+    assert s(FAKE, FAKE, FAKE, 6, 30, 52, 3, 7, 26, 2, 128, 0.0, 1.0, 0.0, FAKE, None, 0, None) == ESHAPE   # 7 !| 30
+    assert s(FAKE, FAKE, FAKE, 6, 30, 52, 3, 30, 25, 2, 128, 0.0, 1.0, 0.0, FAKE, None, 0, None) == ESHAPE  # 25 !| 52
+    assert s(FAKE, FAKE, FAKE, 0, 30, 52, 1, 30, 26, 2, 128, 0.0, 1.0, 0.0, FAKE, None, 0, None) == ESHAPE
+    assert s(FAKE, FAKE, FAKE, 6, 30, 52, 3, 30, 26, 2, 100, 0.0, 1.0, 0.0, FAKE, None, 0, None) == EUNSUP
+    assert s(FAKE, FAKE, FAKE, 2048, 1024, 1024, 2048, 1024, 1024, 1, 64, 0.0, 1.0, 0.0, FAKE, None, 0, None) == ESHAPE
 
 
 def test_stga_shot_workspace_and_argument_errors(lib):
@@ -259,6 +259,6 @@ def test_backward_workspace_and_argument_errors(lib):
     assert b(*args[:17], nbb - 1, None) == EWS
     r = lib.moga_route_backward
     nr = ws(6, 100, 4, 1, 128)
-    assert r(FAKE, FAKE, None, FAKE, None, 100, 128, 4, FAKE, FAKE, None, FAKE, nr, None) == ENULL   # dgate
-    assert r(FAKE, FAKE, None, FAKE, FAKE, 100, 100, 4, FAKE, FAKE, None, FAKE, nr, None) == EUNSUP  # d % 32
-    assert r(FAKE, FAKE, None, FAKE, FAKE, 100, 128, 4, FAKE, FAKE, None, FAKE, nr - 1, None) == EWS
+    assert r(FAKE, FAKE, None, FAKE, None, 100, 128, 4, FAKE, FAKE, None, FAKE, nr, None, 0, None) == ENULL   # dgate
+    assert r(FAKE, FAKE, None, FAKE, FAKE, 100, 100, 4, FAKE, FAKE, None, FAKE, nr, None, 0, None) == EUNSUP  # d % 32
+    assert r(FAKE, FAKE, None, FAKE, FAKE, 100, 128, 4, FAKE, FAKE, None, FAKE, nr - 1, None, 0, None) == EWS
