@@ -506,6 +506,25 @@ def test_backward_lse_and_delta_definitions():
 # Group-balancing statistics (Eq. 6)
 # ---------------------------------------------------------------------------
 
+def check_balance_worked_example():
+    """Eq. 6 by hand on six tokens with gates other than 1 (so that P_i and
+    F_i differ): group ids 0, 2, 0, 1, 2, 2 and gates 0.9, 0.6, 0.7, 0.5,
+    0.8, 0.6, M = 3, alpha = 0.1.  Counts 2, 1, 3 give F = 2/6, 1/6, 3/6; the
+    gate sums 0.9 + 0.7 = 1.6, 0.5 and 0.6 + 0.8 + 0.6 = 2.0, each over N = 6,
+    give P = 1.6/6, 0.5/6, 2.0/6; sum_i F_i P_i = (3.2 + 0.5 + 6.0) / 36 =
+    9.7/36 and L_gb = 0.1 * 3 * 9.7/36 = 2.91/36."""
+    g = np.array([0, 2, 0, 1, 2, 2])
+    gate = np.array([0.9, 0.6, 0.7, 0.5, 0.8, 0.6])
+    F, P, L = oracle.balance_stats(g, gate, 3, 0.1)
+    np.testing.assert_allclose(F, [1 / 3, 1 / 6, 1 / 2], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(P, [1.6 / 6, 0.5 / 6, 2.0 / 6], rtol=0, atol=1e-15)
+    assert abs(L - 2.91 / 36) < 1e-15
+
+
+def test_balance_stats_worked_example():
+    check_balance_worked_example()
+
+
 def test_balance_stats_pages_values():
     with open(os.path.join(GOLDEN, "balance_loss_facts.json")) as f:
         facts = json.load(f)
@@ -594,6 +613,19 @@ def _backward_unscaled_dk(*a, **k):
     return out
 
 
+def _balance_gate_ignored(group_id, gate, M, alpha=0.1):
+    # P_i taken as the token fraction, as if every gate were 1
+    return _orig_balance(group_id, np.ones(np.asarray(gate).shape), M, alpha)
+
+
+def _balance_per_group_mean(group_id, gate, M, alpha=0.1):
+    # P_i as the average gate inside group i (the prose's reading, not Eq. 6's 1/N)
+    F, P, _ = _orig_balance(group_id, gate, M, alpha)
+    P = np.divide(P, F, out=np.zeros_like(P), where=F > 0)
+    return F, P, alpha * M * float(np.sum(F * P))
+
+
+_orig_balance = om.balance_stats
 _orig_permute = om.permute
 _orig_unpermute = om.unpermute
 _orig_shot_windows = om.shot_windows
@@ -611,6 +643,8 @@ MUTANTS = [
     ("moga_backward", _backward_no_delta, [check_backward_autograd]),
     ("moga_backward", _backward_router_sign, [check_backward_autograd]),
     ("moga_backward", _backward_unscaled_dk, [check_backward_autograd]),
+    ("balance_stats", _balance_gate_ignored, [check_balance_worked_example]),
+    ("balance_stats", _balance_per_group_mean, [check_balance_worked_example]),
 ]
 
 
