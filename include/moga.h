@@ -159,6 +159,27 @@ int moga_permute_vt(const int32_t* group_id, const void* Q, const void* K, const
                     int32_t* max_seqlen, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moga_permute_vt_noalloc -- moga_permute_vt for callers that cannot allocate
+ *   device memory (code under HIP graph capture, tight serving loops,
+ *   harnesses that forbid hipMalloc): the same operation, arguments and
+ *   outputs, without the workspace.  The counting sort's scratch (8 * M *
+ *   ceil(N / 1024) bytes of block counts and offsets) lives in a fixed 1 MiB
+ *   device array inside the library, one copy per GPU, held until the
+ *   process ends; sizes that need more return MOGA_ERR_WORKSPACE (M = 64
+ *   allows N <= 2^21, M = 16 every N the transposed-V path supports).  The
+ *   first call on a device looks that device's copy up, with the device
+ *   current (MOGA_ERR_HIP if the lookup fails); no call allocates or frees.
+ *   Every entry of the scratch a call reads is written earlier in the same
+ *   call, so nothing needs clearing between calls, but all calls on one GPU
+ *   share the array: calls that overlap in time on one GPU (several streams
+ *   or host threads) race and must be serialised.
+ */
+int moga_permute_vt_noalloc(const int32_t* group_id, const void* Q, const void* K, const void* V,
+                            int64_t N, int32_t H, int32_t D, int32_t M,
+                            void* Qp, void* Kp, void* Vt, int32_t* perm, int32_t* cu_seqlens,
+                            int32_t* max_seqlen, void* stream);
+
+/*
  * moga_group_attention_unpermute_vt -- moga_group_attention_unpermute with
  *   V given transposed (Vt [H, D, ldv] as written by moga_permute_vt,
  *   padding included; MoGA output equation, Algorithm 1 steps 3 and 4).  Same

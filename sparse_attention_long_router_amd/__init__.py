@@ -12,7 +12,7 @@ from .binding import (MogaForward, MogaTraining, moga_balance_stats, moga_group_
                       moga_unpermute_backward,
                       moga_group_attention_fused, moga_group_attention_unpermute,
                       moga_group_attention_unpermute_vt, moga_group_attention_unpermute_vtq, moga_permute,
-                      moga_permute_vt, moga_route,
+                      moga_permute_vt, moga_permute_vt_noalloc, moga_route,
                       moga_vt_row_length,
                       moga_stga_attention, moga_stga_shot_attention, moga_stga_shot_workspace_bytes, moga_unpermute,
                       moga_workspace_bytes)

@@ -143,13 +143,8 @@ def moga_vt_row_length(N):
     return (N + 63) // 64 * 64 + 64
 
 
-def moga_permute_vt(group_id, M, Q, K, V, Qp=None, Kp=None, Vt=None, perm=None, cu_seqlens=None,
-                    max_seqlen=None, ws=None):
-    """moga_permute with V written transposed per head: Vt bf16 [H, D, ldv]
-    (ldv = moga_vt_row_length(N)), Vt[h, d, j] = V[perm[j], h, d] for j < N,
-    zeros after.  Q = None skips the Q gather (for
-    moga_group_attention_unpermute_vtq, which reads Q through perm).  Returns
-    a dict (Qp, Kp, Vt, perm, cu_seqlens, max_seqlen); Qp is None without Q."""
+def _permute_vt_outputs(group_id, M, Q, K, V, Qp, Kp, Vt, perm, cu_seqlens, max_seqlen):
+    """Checks and (where missing) allocates the outputs of the transposed-V permute."""
     _need(group_id, "group_id", torch.int32, 1)
     N = group_id.shape[0]
     dev = group_id.device
@@ -175,11 +170,38 @@ def moga_permute_vt(group_id, M, Q, K, V, Qp=None, Kp=None, Vt=None, perm=None, 
     _need(perm, "perm", torch.int32, 1, (N,))
     _need(cu_seqlens, "cu_seqlens", torch.int32, 1, (M + 1,))
     _need(max_seqlen, "max_seqlen", torch.int32, 1, (1,))
-    ws, nbytes = _workspace(MOGA_OP_PERMUTE, N, M, H, D, ws, dev)
-    check(_lib.LIB.moga_permute_vt(ptr(group_id), ptr(Q), ptr(K), ptr(V), N, H, D, M, ptr(Qp), ptr(Kp), ptr(Vt),
-                                   ptr(perm), ptr(cu_seqlens), ptr(max_seqlen), ptr(ws), nbytes, stream_handle()),
-          "moga_permute_vt")
     return {"Qp": Qp, "Kp": Kp, "Vt": Vt, "perm": perm, "cu_seqlens": cu_seqlens, "max_seqlen": max_seqlen}
+
+
+def moga_permute_vt(group_id, M, Q, K, V, Qp=None, Kp=None, Vt=None, perm=None, cu_seqlens=None,
+                    max_seqlen=None, ws=None):
+    """moga_permute with V written transposed per head: Vt bf16 [H, D, ldv]
+    (ldv = moga_vt_row_length(N)), Vt[h, d, j] = V[perm[j], h, d] for j < N,
+    zeros after.  Q = None skips the Q gather (for
+    moga_group_attention_unpermute_vtq, which reads Q through perm).  Returns
+    a dict (Qp, Kp, Vt, perm, cu_seqlens, max_seqlen); Qp is None without Q."""
+    out = _permute_vt_outputs(group_id, M, Q, K, V, Qp, Kp, Vt, perm, cu_seqlens, max_seqlen)
+    N, H, D = K.shape
+    ws, nbytes = _workspace(MOGA_OP_PERMUTE, N, M, H, D, ws, group_id.device)
+    check(_lib.LIB.moga_permute_vt(ptr(group_id), ptr(Q), ptr(K), ptr(V), N, H, D, M, ptr(out["Qp"]),
+                                   ptr(out["Kp"]), ptr(out["Vt"]), ptr(out["perm"]), ptr(out["cu_seqlens"]),
+                                   ptr(out["max_seqlen"]), ptr(ws), nbytes, stream_handle()),
+          "moga_permute_vt")
+    return out
+
+
+def moga_permute_vt_noalloc(group_id, M, Q, K, V, Qp=None, Kp=None, Vt=None, perm=None, cu_seqlens=None,
+                            max_seqlen=None):
+    """moga_permute_vt without a workspace: the library keeps the sort's
+    scratch in a fixed per-GPU device array (see include/moga.h).  Pass every
+    output to have no allocation at all; missing ones are allocated here."""
+    out = _permute_vt_outputs(group_id, M, Q, K, V, Qp, Kp, Vt, perm, cu_seqlens, max_seqlen)
+    N, H, D = K.shape
+    check(_lib.LIB.moga_permute_vt_noalloc(ptr(group_id), ptr(Q), ptr(K), ptr(V), N, H, D, M, ptr(out["Qp"]),
+                                           ptr(out["Kp"]), ptr(out["Vt"]), ptr(out["perm"]),
+                                           ptr(out["cu_seqlens"]), ptr(out["max_seqlen"]), stream_handle()),
+          "moga_permute_vt_noalloc")
+    return out
 
 
 def moga_group_attention_unpermute_vt(Qp, Kp, Vt, cu_seqlens, perm, gate, softmax_scale=0.0, beta=0.0, O=None,

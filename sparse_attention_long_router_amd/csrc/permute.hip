@@ -20,7 +20,16 @@
 // alone, for an attention that reads Q through perm) and writes V transposed
 // per head (gather_vt_kernel): Vt[h][d][j], the layout whose 64-key tiles the
 // attention reads with one 16-byte LDS read per MFMA operand.
+#include <mutex>
+
 #include "moga_internal.h"
+
+// Sort scratch of moga_permute_vt_noalloc (the [M][blocks] counts and base
+// offsets of the counting sort): a fixed device array, one copy per GPU,
+// held until the process ends.  In host code `scratch` only names the symbol;
+// its device address comes from hipGetSymbolAddress (scratch_address below).
+constexpr size_t kNoAllocScratchBytes = size_t(1) << 20;  // 1 MiB
+static __device__ __align__(256) int32_t scratch[kNoAllocScratchBytes / sizeof(int32_t)];
 
 namespace moga {
 namespace {
@@ -248,14 +257,51 @@ extern "C" int moga_permute(const int32_t* group_id, const void* Q, const void* 
   return MOGA_OK;
 }
 
-extern "C" int moga_permute_vt(const int32_t* group_id, const void* Q, const void* K, const void* V, int64_t N,
-                               int32_t H, int32_t D, int32_t M, void* Qp, void* Kp, void* Vt, int32_t* perm,
-                               int32_t* cu_seqlens, int32_t* max_seqlen, void* ws, size_t ws_bytes, void* stream) {
-  using namespace moga;
+namespace moga {
+namespace {
+int permute_vt_args(const int32_t* group_id, const void* Q, const void* K, const void* V, int64_t N, int32_t H,
+                    int32_t D, int32_t M, const void* Qp, const void* Kp, const void* Vt, const int32_t* perm,
+                    const int32_t* cu_seqlens, const int32_t* max_seqlen) {
   if (!group_id || !perm || !cu_seqlens || !max_seqlen || !K || !V || !Kp || !Vt) return MOGA_ERR_NULL;
   if (!Q != !Qp) return MOGA_ERR_NULL;  // Q is gathered only when both are given
   if (N < 1 || N >= (int64_t(1) << 31) || M < 1 || H < 1 || D < 1) return MOGA_ERR_SHAPE;
   if (M > kMaxGroups || !valid_head_dims(H, D) || N > kVtMaxTokens) return MOGA_ERR_UNSUPPORTED;
+  return MOGA_OK;
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept for the process.
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];
+
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return MOGA_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return MOGA_ERR_HIP;
+    }
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return MOGA_OK;
+}
+}  // namespace
+}  // namespace moga
+
+extern "C" int moga_permute_vt(const int32_t* group_id, const void* Q, const void* K, const void* V, int64_t N,
+                               int32_t H, int32_t D, int32_t M, void* Qp, void* Kp, void* Vt, int32_t* perm,
+                               int32_t* cu_seqlens, int32_t* max_seqlen, void* ws, size_t ws_bytes, void* stream) {
+  using namespace moga;
+  const int arg = permute_vt_args(group_id, Q, K, V, N, H, D, M, Qp, Kp, Vt, perm, cu_seqlens, max_seqlen);
+  if (arg != MOGA_OK) return arg;
   // the sort, as moga_permute without row copies
   const int rc = moga_permute(group_id, nullptr, nullptr, nullptr, N, H, D, M, nullptr, nullptr, nullptr, perm,
                               cu_seqlens, max_seqlen, ws, ws_bytes, stream);
@@ -281,4 +327,18 @@ extern "C" int moga_permute_vt(const int32_t* group_id, const void* Q, const voi
                                               static_cast<uint16_t*>(Vt));
   MOGA_LAUNCH_CHECK();
   return MOGA_OK;
+}
+
+extern "C" int moga_permute_vt_noalloc(const int32_t* group_id, const void* Q, const void* K, const void* V,
+                                       int64_t N, int32_t H, int32_t D, int32_t M, void* Qp, void* Kp, void* Vt,
+                                       int32_t* perm, int32_t* cu_seqlens, int32_t* max_seqlen, void* stream) {
+  using namespace moga;
+  const int arg = permute_vt_args(group_id, Q, K, V, N, H, D, M, Qp, Kp, Vt, perm, cu_seqlens, max_seqlen);
+  if (arg != MOGA_OK) return arg;
+  if (moga_workspace_bytes(MOGA_OP_PERMUTE, N, M, H, D) > kNoAllocScratchBytes) return MOGA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const int rc = scratch_address(&ws);
+  if (rc != MOGA_OK) return rc;
+  return moga_permute_vt(group_id, Q, K, V, N, H, D, M, Qp, Kp, Vt, perm, cu_seqlens, max_seqlen, ws,
+                         kNoAllocScratchBytes, stream);
 }

@@ -43,6 +43,11 @@ int main() {
          "permute_vt Q without Qp");
   expect(moga_permute_vt(I, P, P, P, (int64_t(1) << 23), 2, 128, 4, P, P, P, I, I, I, P, big, nullptr),
          MOGA_ERR_UNSUPPORTED, "permute_vt N");
+  expect(moga_permute_vt_noalloc(I, P, P, P, N, 2, 128, 4, nullptr, P, P, I, I, I, nullptr), MOGA_ERR_NULL,
+         "permute_vt_noalloc Q without Qp");
+  expect(moga_permute_vt_noalloc(I, nullptr, P, P, (int64_t(1) << 21) + 1024, 2, 128, 64, nullptr, P, P, I, I, I,
+                                 nullptr),
+         MOGA_ERR_WORKSPACE, "permute_vt_noalloc beyond its scratch");
 
   expect(moga_group_attention(P, P, P, I, N, 2, 128, 4, 0.f, P, P, 0, nullptr), MOGA_ERR_WORKSPACE,
          "attention ws");

@@ -33,7 +33,7 @@ def declared_symbols():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(lib, n), n
     from sparse_attention_long_router_amd import _lib
@@ -200,6 +200,28 @@ def test_unpermute_argument_errors(lib):
     assert u(FAKE, FAKE, None, 10, 2, 64, 0.0, FAKE, None) == ENULL
     assert u(FAKE, FAKE, FAKE, -1, 2, 64, 0.0, FAKE, None) == ESHAPE
     assert u(FAKE, FAKE, FAKE, 10, 2, 32, 0.0, FAKE, None) == EUNSUP
+
+
+def test_permute_noalloc_argument_errors(lib):
+    """Argument and size errors come back before any device call (no GPU here)."""
+    p = lib.moga_permute_vt_noalloc
+    args = dict(g=FAKE, Q=None, K=FAKE, V=FAKE, N=100, H=2, D=128, M=4, Qp=None, Kp=FAKE, Vt=FAKE,
+                perm=FAKE, cu=FAKE, mx=FAKE)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return p(a["g"], a["Q"], a["K"], a["V"], a["N"], a["H"], a["D"], a["M"], a["Qp"], a["Kp"], a["Vt"],
+                 a["perm"], a["cu"], a["mx"], None)
+
+    assert call(g=None) == ENULL
+    assert call(Q=FAKE) == ENULL                     # Q without Qp
+    assert call(N=0) == ESHAPE
+    assert call(M=65) == EUNSUP
+    assert call(D=96) == EUNSUP
+    assert call(N=(1 << 23)) == EUNSUP               # beyond the transposed-V layout
+    # the fixed 1 MiB sort scratch: 8 * M * ceil(N / 1024) bytes at most
+    assert call(N=(1 << 21) + 1024, M=64) == EWS
+    assert call(N=(1 << 22), M=33) == EWS
 
 
 def test_stga_argument_errors(lib):
