@@ -63,7 +63,10 @@ constexpr int kBN = 64;                             // keys per LDS tile
 // this reads 6.0 GB from HBM per launch against 10.5 GB with runs of 8, in
 // the same time.
 constexpr int kXcdRun = 32;
-constexpr int kTabKeys = 8192;                      // key-row table entries (index-map windows)
+// Key-row table entries of an index-map window (16 KB of LDS beside the four
+// K/V buffers): the static windows hold 2,340 keys, the shot-aware ones up to
+// (win_t + 2 augment) tiles; larger windows evaluate the map per load.
+constexpr int kTabKeys = 4096;
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -152,6 +155,7 @@ struct StgaRows {
   static constexpr bool kTable = true;  // key rows tabulated in LDS once per item
   static constexpr bool kVt = false;
   int Hs, Ws, win_t, tile_h, tile_w, nty, ntx, tiles_per_group, H, items;
+  uint32_t tab_bytes;  // byte size of one K/V tensor when below 2^31 (key table of byte offsets), else 0
   __device__ __forceinline__ bool decode(int item, Work& w) const {
     if (item >= items) return false;
     const int per_group = H * tiles_per_group;
@@ -201,6 +205,7 @@ struct ShotRows {
   const ShotWindow* win;
   const int* nwin;
   int Hs, Ws, tile_h, tile_w, ntx, nspatial, tpg, H;
+  uint32_t tab_bytes;  // as in StgaRows
   __device__ __forceinline__ bool decode(int item, Work& w) const {
     const int per_win = nspatial * H * tpg;
     const int wi = item / per_win;
@@ -327,6 +332,25 @@ __device__ __forceinline__ void issue_tile_tab(const uint16_t* __restrict__ K, c
                                      16, 0, 0);
     __builtin_amdgcn_global_load_lds((global_void*)(V + base + (p ^ vswz(r, CPR)) * 8), (lds_void*)(Vs + lds_off),
                                      16, 0, 0);
+  }
+}
+
+// Byte-offset table variant: tab holds each key's row offset in bytes (padded
+// to whole tiles), the tensors are covered by one buffer descriptor each and
+// the head offset rides in the scalar offset.
+template <int D, int NW>
+__device__ __forceinline__ void issue_tile_tab32(i32x4v krs, i32x4v vrs, uint16_t* Ks, uint16_t* Vs,
+                                                 const int32_t* tab, int soff, int k0, int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int LOADS = kBN * CPR / (NW * kWave);
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) {
+    const int q = (wave * LOADS + j) * kWave + lane;
+    const int r = q / CPR, p = q % CPR;
+    const int off = tab[k0 + r];
+    const int lds_off = (wave * LOADS + j) * kWave * 8;
+    raw_buffer_load_lds(krs, (lds_void*)(Ks + lds_off), 16, off + ((p ^ kswz(r, CPR)) << 4), soff, 0, 0);
+    raw_buffer_load_lds(vrs, (lds_void*)(Vs + lds_off), 16, off + ((p ^ vswz(r, CPR)) << 4), soff, 0, 0);
   }
 }
 
@@ -625,7 +649,7 @@ struct Epilogue {
 };
 
 template <int D, int QB, class Rows, int kEpi>
-__global__ __launch_bounds__(waves_for<QB>() * kWave) void attn_kernel(
+__global__ __launch_bounds__(waves_for<QB>() * kWave, 2) void attn_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, int64_t row_stride, float scale_log2, Epilogue epi, Rows rows) {
   constexpr int KSTEPS = D / 16;
@@ -639,7 +663,7 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave) void attn_kernel(
   // keep two: their key-row table needs the LDS).  K buffers first, so that
   // every K read (and every V read) is one base address plus an offset below
   // 64 KB.
-  constexpr bool kPair = !Rows::kTable;
+  constexpr bool kPair = true;
   constexpr int NBUF = kPair ? 4 : 2;
   __shared__ __attribute__((aligned(1024))) uint16_t kv_lds[2 * NBUF][kBN * D];
   uint16_t* const Ks0 = kv_lds[0];
@@ -664,9 +688,17 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave) void attn_kernel(
   // Index-map windows: tabulate every key's token row once (up to kTabKeys).
   __shared__ int32_t ktab[Rows::kTable ? kTabKeys : 1];
   [[maybe_unused]] const bool use_tab = Rows::kTable && w.len <= kTabKeys;  // uniform per block
+  [[maybe_unused]] bool use_tab32 = false;
+  if constexpr (Rows::kTable) use_tab32 = use_tab && rows.tab_bytes != 0;
   if constexpr (Rows::kTable) {
     if (use_tab) {
-      for (int i = tid; i < w.len; i += NW * kWave) ktab[i] = (int32_t)rows.key(w, i);
+      if (use_tab32) {  // byte offsets of the rows, padded to whole tiles with the last row
+        const int padded = (w.len + kBN - 1) / kBN * kBN;
+        for (int i = tid; i < padded; i += NW * kWave)
+          ktab[i] = (int32_t)(rows.key(w, i < w.len ? i : w.len - 1) * row_stride * 2);
+      } else {
+        for (int i = tid; i < w.len; i += NW * kWave) ktab[i] = (int32_t)rows.key(w, i);
+      }
       __syncthreads();
     }
   }
@@ -691,7 +723,12 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave) void attn_kernel(
       issue_tile_idx<D, NW>(K, V, Kd, Vd, kidx, row_stride, hoff, wave, lane);
       if (t + 1 < ntiles) fetch_keys<D, NW>(rows, w, (t + 1) * kBN, wave, lane, kidx);
     } else if (use_tab) {
-      issue_tile_tab<D, NW>(K, V, Kd, Vd, ktab, w.len, row_stride, hoff, t * kBN, wave, lane);
+      if (use_tab32)
+        issue_tile_tab32<D, NW>(row_range_rsrc(K, 1, 0, (int)rows.tab_bytes),
+                                row_range_rsrc(V, 1, 0, (int)rows.tab_bytes), Kd, Vd, ktab, (int)(hoff * 2),
+                                t * kBN, wave, lane);
+      else
+        issue_tile_tab<D, NW>(K, V, Kd, Vd, ktab, w.len, row_stride, hoff, t * kBN, wave, lane);
     } else {
       issue_tile<D, NW>(K, V, Kd, Vd, rows, w, row_stride, hoff, t * kBN, wave, lane);
     }
@@ -752,7 +789,7 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave) void attn_kernel(
   // or kStats (row maxima and sums into mx, lsum).
   constexpr int kStats = 3;
   float mx[QB], lsum[QB];
-  auto run = [&](auto mode) {
+  auto run = [&](auto mode) __attribute__((always_inline)) {
     constexpr int kMode = decltype(mode)::value;
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
@@ -1046,6 +1083,14 @@ __global__ __launch_bounds__(kShotThreads) void shot_windows_kernel(const int32_
   if (tid == 0) *nwin = min(base, max_windows);
 }
 
+// Byte size of one [N, H, D] bf16 tensor if it is below 2^31 (the index-map
+// windows then read rows through a buffer descriptor at 32-bit byte offsets),
+// else 0.
+inline uint32_t table_bytes(int64_t N, int32_t H, int32_t D) {
+  const int64_t b = N * H * D * 2;
+  return b < (int64_t(1) << 31) ? (uint32_t)b : 0u;
+}
+
 template <int D, class Rows, int kEpi>
 int launch_attn(const void* Q, const void* K, const void* V, void* O, int64_t row_stride, float scale,
                 Epilogue epi, Rows rows, int64_t items_bound, hipStream_t st) {
@@ -1101,7 +1146,7 @@ extern "C" int moga_stga_attention(const void* Q, const void* K, const void* V, 
   const int tpg = (int)ceil_div(gsize, kBM);
   const int64_t items = (N / gsize) * H * tpg;
   if (items > 0x7fffffff) return MOGA_ERR_SHAPE;
-  StgaRows rows{Hs, Ws, win_t, tile_h, tile_w, Hs / tile_h, Ws / tile_w, tpg, H, (int)items};
+  StgaRows rows{Hs, Ws, win_t, tile_h, tile_w, Hs / tile_h, Ws / tile_w, tpg, H, (int)items, table_bytes(N, H, D)};
   hipStream_t st = as_stream(stream);
   const Epilogue epi{alpha, beta, nullptr, nullptr, nullptr, 0};
   if (D == 128) return launch_attn<128, StgaRows, kEpiScaled>(Q, K, V, O, (int64_t)H * D, scale, epi, rows, items, st);
@@ -1212,7 +1257,7 @@ extern "C" int moga_stga_shot_attention(const void* Q, const void* K, const void
   auto* win = reinterpret_cast<ShotWindow*>(static_cast<char*>(ws) + 256);
   shot_windows_kernel<<<1, kShotThreads, 0, st>>>(shot_start, n_shots, T, win_t, augment, max_windows, win, nwin);
   MOGA_LAUNCH_CHECK();
-  ShotRows rows{win, nwin, Hs, Ws, tile_h, tile_w, ntx, nspatial, tpg, H};
+  ShotRows rows{win, nwin, Hs, Ws, tile_h, tile_w, ntx, nspatial, tpg, H, table_bytes(N, H, D)};
   const Epilogue epi{alpha, beta, nullptr, nullptr, nullptr, 0};
   if (D == 128) return launch_attn<128, ShotRows, kEpiScaled>(Q, K, V, O, (int64_t)H * D, scale, epi, rows, items, st);
   return launch_attn<64, ShotRows, kEpiScaled>(Q, K, V, O, (int64_t)H * D, scale, epi, rows, items, st);
