@@ -169,7 +169,8 @@ def cpu_baseline(inp, wl, counts, rows_per_group):
         "sample": (f"route + permute over all {wl.N} tokens ({t_route:.2f} s); attention of {rows.size} "
                    f"sampled query rows (first, last and {rows_per_group} random per group) x {wl.H} heads "
                    f"({t_attn:.2f} s, {sample_flops / 1e9:.1f} GFLOP), extrapolated by FLOPs to the full step "
-                   f"({t_full:.1f} s); float64 NumPy on {blas}, {threads} BLAS threads, "
+                   f"({t_full:.1f} s; the sample is bounded so that the default run finishes in about a minute); "
+                   f"float64 NumPy on {blas}, {threads} BLAS threads, "
                    f"{len(os.sched_getaffinity(0))} cores visible, {cpu}"),
     }
 
