@@ -148,6 +148,24 @@ struct MogaPermRows {
   __device__ __forceinline__ int32_t key_index(const Work& w, int i) const { return perm[w.row0 + i]; }
 };
 
+// i / d and i % d for 0 <= i < 2^24 and 0 < d < 2^24 from a float reciprocal
+// of d (rounded once): the float quotient is within 1 of the exact one and a
+// single correction step fixes it.  Cheaper than the integer division
+// sequence in the per-item key tables of the index-map windows.
+__device__ __forceinline__ int fast_divmod(int i, int d, float inv_d, int& rem) {
+  int q = (int)((float)i * inv_d);
+  int r = i - q * d;
+  if (r < 0) {
+    --q;
+    r += d;
+  } else if (r >= d) {
+    ++q;
+    r -= d;
+  }
+  rem = r;
+  return q;
+}
+
 // Static windows over frame-major tokens n = (t*Hs + y)*Ws + x.
 struct StgaRows {
   static constexpr bool kIndirect = false;
@@ -156,6 +174,7 @@ struct StgaRows {
   static constexpr bool kVt = false;
   int Hs, Ws, win_t, tile_h, tile_w, nty, ntx, tiles_per_group, H, items;
   uint32_t tab_bytes;  // byte size of one K/V tensor when below 2^31 (key table of byte offsets), else 0
+  float inv_area, inv_tw;  // 1 / (tile_h * tile_w), 1 / tile_w
   __device__ __forceinline__ bool decode(int item, Work& w) const {
     if (item >= items) return false;
     const int per_group = H * tiles_per_group;
@@ -175,11 +194,9 @@ struct StgaRows {
     return true;
   }
   __device__ __forceinline__ int64_t row(const Work& w, int i) const {
-    const int area = tile_h * tile_w;
-    const int tt = i / area;
-    const int rem = i - tt * area;
-    const int yy = rem / tile_w;
-    const int xx = rem - yy * tile_w;
+    int rem, xx;
+    const int tt = fast_divmod(i, tile_h * tile_w, inv_area, rem);
+    const int yy = fast_divmod(rem, tile_w, inv_tw, xx);
     return ((int64_t)(w.t0 + tt) * Hs + (w.y0 + yy)) * Ws + (w.x0 + xx);
   }
   __device__ __forceinline__ int64_t key(const Work& w, int i) const { return row(w, i); }
@@ -206,6 +223,7 @@ struct ShotRows {
   const int* nwin;
   int Hs, Ws, tile_h, tile_w, ntx, nspatial, tpg, H;
   uint32_t tab_bytes;  // as in StgaRows
+  float inv_area, inv_tw;  // as in StgaRows
   __device__ __forceinline__ bool decode(int item, Work& w) const {
     const int per_win = nspatial * H * tpg;
     const int wi = item / per_win;
@@ -233,22 +251,22 @@ struct ShotRows {
     return true;
   }
   __device__ __forceinline__ int64_t at(const Work& w, int frame, int i) const {
-    const int yy = i / tile_w;
-    const int xx = i - yy * tile_w;
+    int xx;
+    const int yy = fast_divmod(i, tile_w, inv_tw, xx);
     return ((int64_t)frame * Hs + (w.y0 + yy)) * Ws + (w.x0 + xx);
   }
   __device__ __forceinline__ int64_t row(const Work& w, int i) const {
-    const int area = tile_h * tile_w;
-    const int tt = i / area;
-    return at(w, w.t0 + tt, i - tt * area);
+    int rem;
+    const int tt = fast_divmod(i, tile_h * tile_w, inv_area, rem);
+    return at(w, w.t0 + tt, rem);
   }
   __device__ __forceinline__ int64_t key(const Work& w, int i) const {
-    const int area = tile_h * tile_w;
-    const int tt = i / area;
+    int rem;
+    const int tt = fast_divmod(i, tile_h * tile_w, inv_area, rem);
     const int t0 = w.t0, pre_off = w.pre_off, nxt_off = w.nxt_off;  // values, not a select of field addresses
     const int off = tt < w.npre ? pre_off : nxt_off;
     const int frame = tt + (tt < w.nt ? t0 : off);
-    return at(w, frame, i - tt * area);
+    return at(w, frame, rem);
   }
 };
 
@@ -982,6 +1000,17 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave, 2) void attn_kernel(
       keep = epi.beta;
     }
     uint16_t* op = O + orow * row_stride + hoff;
+    // STGA with beta != 0 (a branch summed onto another): every old value of
+    // the row is loaded before any is used, so the row costs one memory
+    // latency rather than one per 8-byte piece
+    u32x2 prev[DBLK][4];
+    const bool acc = kEpi != kEpiPlain && keep != 0.f;  // uniform
+    if (kEpi == kEpiScaled && acc) {
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) prev[db][q4] = *reinterpret_cast<const u32x2*>(op + 32 * db + 8 * q4 + 4 * hh);
+    }
 #pragma unroll
     for (int db = 0; db < DBLK; ++db)
 #pragma unroll
@@ -989,8 +1018,8 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave, 2) void attn_kernel(
         const int d0 = 32 * db + 8 * q4 + 4 * hh;
         float v0 = o[b][db][4 * q4] * scale, v1 = o[b][db][4 * q4 + 1] * scale;
         float v2 = o[b][db][4 * q4 + 2] * scale, v3 = o[b][db][4 * q4 + 3] * scale;
-        if (kEpi != kEpiPlain && keep != 0.f) {
-          const u32x2 old = *reinterpret_cast<const u32x2*>(op + d0);
+        if (acc) {
+          const u32x2 old = kEpi == kEpiScaled ? prev[db][q4] : *reinterpret_cast<const u32x2*>(op + d0);
           v0 += keep * bf16_lo(old[0]); v1 += keep * bf16_hi(old[0]);
           v2 += keep * bf16_lo(old[1]); v3 += keep * bf16_hi(old[1]);
         }
@@ -1146,7 +1175,8 @@ extern "C" int moga_stga_attention(const void* Q, const void* K, const void* V, 
   const int tpg = (int)ceil_div(gsize, kBM);
   const int64_t items = (N / gsize) * H * tpg;
   if (items > 0x7fffffff) return MOGA_ERR_SHAPE;
-  StgaRows rows{Hs, Ws, win_t, tile_h, tile_w, Hs / tile_h, Ws / tile_w, tpg, H, (int)items, table_bytes(N, H, D)};
+  StgaRows rows{Hs, Ws, win_t, tile_h, tile_w, Hs / tile_h, Ws / tile_w, tpg, H, (int)items, table_bytes(N, H, D),
+                1.0f / (float)(tile_h * tile_w), 1.0f / (float)tile_w};
   hipStream_t st = as_stream(stream);
   const Epilogue epi{alpha, beta, nullptr, nullptr, nullptr, 0};
   if (D == 128) return launch_attn<128, StgaRows, kEpiScaled>(Q, K, V, O, (int64_t)H * D, scale, epi, rows, items, st);
@@ -1257,7 +1287,8 @@ extern "C" int moga_stga_shot_attention(const void* Q, const void* K, const void
   auto* win = reinterpret_cast<ShotWindow*>(static_cast<char*>(ws) + 256);
   shot_windows_kernel<<<1, kShotThreads, 0, st>>>(shot_start, n_shots, T, win_t, augment, max_windows, win, nwin);
   MOGA_LAUNCH_CHECK();
-  ShotRows rows{win, nwin, Hs, Ws, tile_h, tile_w, ntx, nspatial, tpg, H, table_bytes(N, H, D)};
+  ShotRows rows{win, nwin, Hs, Ws, tile_h, tile_w, ntx, nspatial, tpg, H, table_bytes(N, H, D),
+                1.0f / (float)(tile_h * tile_w), 1.0f / (float)tile_w};
   const Epilogue epi{alpha, beta, nullptr, nullptr, nullptr, 0};
   if (D == 128) return launch_attn<128, ShotRows, kEpiScaled>(Q, K, V, O, (int64_t)H * D, scale, epi, rows, items, st);
   return launch_attn<64, ShotRows, kEpiScaled>(Q, K, V, O, (int64_t)H * D, scale, epi, rows, items, st);
