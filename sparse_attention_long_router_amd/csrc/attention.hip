@@ -11,13 +11,16 @@
 // Work item = (group, head, tile of 256 queries), one workgroup each.  A wave
 // owns QB blocks of 32 queries (QB = 1: 8 waves, two per SIMD, so the
 // hardware interleaves one wave's softmax with the other's MFMAs; QB = 2:
-// 4 waves, one per SIMD, each K/V operand read feeding two MFMAs).  Per
-// 64-key tile:
+// 4 waves, one per SIMD, each K/V operand read feeding two MFMAs).  The static
+// STGA windows use items of 128 queries instead (4 waves, two workgroups per
+// CU): their items are short (2,340 keys in the long-video setting), and the
+// second workgroup keeps the matrix cores busy through one item's table build,
+// Q loads and output stores.  Per 64-key tile:
 //   K and V rows arrive in LDS by 16-byte direct-to-LDS loads, XOR-swizzled
 //   at 16-byte granularity (conflict-free reads), into four buffers with one
 //   barrier per two tiles (the next pair streams in while this one computes;
-//   index-map windows, whose key-row table needs the LDS, keep two buffers
-//   and one barrier per tile); a tile's loads are issued after the first K
+//   the 128-query items, two workgroups to a CU's LDS, keep two buffers and
+//   one barrier per tile); a tile's loads are issued after the first K
 //   operand reads of the tile before it;
 //   S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = the
 //   wave's Q fragment held in registers) -- the C layout gives every lane one
@@ -53,20 +56,29 @@ __device__ void raw_buffer_load_lds(i32x4v rsrc, __attribute__((address_space(3)
 namespace moga {
 namespace {
 
-constexpr int kBM = 256;  // queries per workgroup (work item)
+constexpr int kBM = 256;  // queries per work item of the learned groups
 constexpr int kQB = MOGA_ATTN_QB;                   // 32-query blocks per wave (1 or 2)
-template <int QB>
-constexpr int waves_for() { return kBM / (32 * QB); }
+// Waves per workgroup: Rows::kQueries queries per work item, 32 * QB per wave.
+template <class Rows, int QB>
+constexpr int waves_for() { return Rows::kQueries / (32 * QB); }
 constexpr int kBN = 64;                             // keys per LDS tile
 // Consecutive items per XCD: 32, one per CU of the XCD, so a whole XCD
 // streams one (group, head)'s K/V together through its L2.  At 190k tokens
 // this reads 6.0 GB from HBM per launch against 10.5 GB with runs of 8, in
 // the same time.
 constexpr int kXcdRun = 32;
-// Key-row table entries of an index-map window (16 KB of LDS beside the four
-// K/V buffers): the static windows hold 2,340 keys, the shot-aware ones up to
-// (win_t + 2 augment) tiles; larger windows evaluate the map per load.
-constexpr int kTabKeys = 4096;
+// Key-row table entries of an index-map window (Rows::kTabKeys): 4,096
+// (16 KB of LDS beside the four K/V buffers) for the shot-aware windows, which
+// reach (win_t + 2 augment) frames of a tile; 3,840 for the static windows
+// (2,340 keys in the long-video setting), whose two workgroups per CU share
+// the LDS.  Larger windows evaluate the map per load.
+template <class Rows>
+constexpr int tab_keys() {
+  if constexpr (Rows::kTable)
+    return Rows::kTabKeys;
+  else
+    return 1;
+}
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -82,6 +94,7 @@ struct Work {
 
 // Learned groups: rows of group g are cu[g] .. cu[g+1]-1 of the permuted tensors.
 struct MogaRows {
+  static constexpr int kQueries = kBM;
   static constexpr bool kIndirect = false;
   static constexpr bool kContiguous = true;  // key row i of a group is row0 + i
   static constexpr bool kTable = false;
@@ -114,6 +127,7 @@ struct MogaRows {
 // of one channel contiguous and zero-padded (moga_permute_vt writes it).  A V operand of the
 // P V product is then one 16-byte LDS read instead of two transposing reads.
 struct MogaVtRows {
+  static constexpr int kQueries = kBM;
   static constexpr bool kIndirect = false;
   [[maybe_unused]] static constexpr bool kContiguous = true;  // as MogaRows; the kVt path takes precedence
   static constexpr bool kTable = false;
@@ -137,6 +151,7 @@ struct MogaVtQRows : MogaVtRows {
 // original token perm[j], so Q, K and V are the unpermuted tensors and no
 // gathered copies exist.  Key rows are fetched a tile ahead (kIndirect).
 struct MogaPermRows {
+  static constexpr int kQueries = kBM;
   static constexpr bool kIndirect = true;
   static constexpr bool kContiguous = false;
   static constexpr bool kTable = false;
@@ -168,6 +183,10 @@ __device__ __forceinline__ int fast_divmod(int i, int d, float inv_d, int& rem) 
 
 // Static windows over frame-major tokens n = (t*Hs + y)*Ws + x.
 struct StgaRows {
+  // 128-query items (four waves): two workgroups share a CU, so one item's
+  // table, Q loads and output stores overlap the other's tiles.
+  static constexpr int kQueries = 128;
+  static constexpr int kTabKeys = 3840;
   static constexpr bool kIndirect = false;
   static constexpr bool kContiguous = false;
   static constexpr bool kTable = true;  // key rows tabulated in LDS once per item
@@ -181,7 +200,7 @@ struct StgaRows {
     const int grp = item / per_group;
     const int rem = item - grp * per_group;
     w.head = rem / tiles_per_group;
-    w.q0 = (rem - w.head * tiles_per_group) * kBM;
+    w.q0 = (rem - w.head * tiles_per_group) * kQueries;
     w.len = win_t * tile_h * tile_w;
     w.nq = w.len;
     const int tw = grp / (nty * ntx);
@@ -215,6 +234,8 @@ struct ShotWindow {
 // Items: window-major, then spatial tile, head and query tile, so the query
 // tiles sharing one key set are consecutive (and land on one XCD).
 struct ShotRows {
+  static constexpr int kQueries = kBM;
+  static constexpr int kTabKeys = 4096;
   static constexpr bool kIndirect = false;
   static constexpr bool kContiguous = false;
   static constexpr bool kTable = true;
@@ -232,7 +253,7 @@ struct ShotRows {
     const int sp = rem / (H * tpg);
     rem -= sp * (H * tpg);
     w.head = rem / tpg;
-    w.q0 = (rem - w.head * tpg) * kBM;
+    w.q0 = (rem - w.head * tpg) * kQueries;
     const ShotWindow sw = win[wi];
     const int area = tile_h * tile_w;
     w.nq = sw.nt * area;
@@ -528,8 +549,11 @@ __device__ __forceinline__ void qk_half(const uint16_t* Ks, const bf16x8 (&qf)[Q
 }
 
 // O^T += V^T P^T for one 32-key half kb and the wave's query blocks; each V^T
-// operand (two transposing LDS reads) feeds QB MFMAs.
-template <int D, int QB>
+// operand (two transposing LDS reads) feeds QB MFMAs.  kOneOffset forms each
+// read address as the buffer plus one offset: with the V buffers in their own
+// arrays this keeps the reads traceable to their buffer, so the compiler does
+// not wait for the loads in flight into the other buffer.
+template <int D, int QB, bool kOneOffset = false>
 __device__ __forceinline__ void pv_half(const uint16_t* Vs, const bf16x8 (&p)[QB][2], int kb, int lane,
                                         f32x16 (&o)[QB][D / 32]) {
   constexpr int CPR = D / 8;
@@ -543,10 +567,12 @@ __device__ __forceinline__ void pv_half(const uint16_t* Vs, const bf16x8 (&p)[QB
     for (int db = 0; db < D / 32; ++db) {
       const int col = 32 * db + 16 * tr_g + 4 * tr_q;
       const int ch = col >> 3, within = col & 7;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(Vs + r1 * D + ((ch ^ vswz(r1, CPR)) << 3) + within));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(Vs + r2 * D + ((ch ^ vswz(r2, CPR)) << 3) + within));
+      const uint16_t* a1 = kOneOffset ? Vs + (r1 * D + ((ch ^ vswz(r1, CPR)) << 3) + within)
+                                      : Vs + r1 * D + ((ch ^ vswz(r1, CPR)) << 3) + within;
+      const uint16_t* a2 = kOneOffset ? Vs + (r2 * D + ((ch ^ vswz(r2, CPR)) << 3) + within)
+                                      : Vs + r2 * D + ((ch ^ vswz(r2, CPR)) << 3) + within;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a1);
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a2);
       const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
       for (int b = 0; b < QB; ++b) o[b][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[b][t], o[b][db], 0, 0, 0);
@@ -591,7 +617,7 @@ __device__ __forceinline__ void mask_half(f32x16 (&s)[QB], int key0, int len, in
 
 // One 64-key tile for the wave's query blocks, in 32-key halves:
 //   QK(h0) QK(h1) | softmax(h0) PV(h0) | softmax(h1) PV(h1)
-template <int D, int QB, bool kMask, bool kVt, int kExp, class AfterLoads = NoOp>
+template <int D, int QB, bool kMask, bool kVt, int kExp, bool kOneOffset = false, class AfterLoads = NoOp>
 __device__ __forceinline__ void tile_step(const uint16_t* Ks, const uint16_t* Vs, int k0, int len,
                                           const bf16x8 (&qf)[QB][D / 16], f32x16 (&o)[QB][D / 32],
                                           RowState (&rs)[QB], float scale_log2, int lane,
@@ -611,14 +637,14 @@ __device__ __forceinline__ void tile_step(const uint16_t* Ks, const uint16_t* Vs
   if constexpr (kVt)
     pv_half_t<D, QB>(Vs, p, 0, lane, o);
   else
-    pv_half<D, QB>(Vs, p, 0, lane, o);
+    pv_half<D, QB, kOneOffset>(Vs, p, 0, lane, o);
   mask_half<kMask, QB, kVt>(s1, k0 + 32, len, hh);
 #pragma unroll
   for (int b = 0; b < QB; ++b) softmax_half<kExp>(s1[b], rs[b], scale_log2, p[b]);
   if constexpr (kVt)
     pv_half_t<D, QB>(Vs, p, 1, lane, o);
   else
-    pv_half<D, QB>(Vs, p, 1, lane, o);
+    pv_half<D, QB, kOneOffset>(Vs, p, 1, lane, o);
 }
 
 // Row maxima and sums (the first pass of the exact recomputation): per lane
@@ -667,27 +693,39 @@ struct Epilogue {
 };
 
 template <int D, int QB, class Rows, int kEpi>
-__global__ __launch_bounds__(waves_for<QB>() * kWave, 2) void attn_kernel(
+__global__ __launch_bounds__((waves_for<Rows, QB>() * kWave), 2) void attn_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, int64_t row_stride, float scale_log2, Epilogue epi, Rows rows) {
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
-  constexpr int NW = waves_for<QB>();
+  constexpr int NW = waves_for<Rows, QB>();
   // The Q fragments carry the softmax scale in log2 units, except in the
   // training forward: its saved log-sum-exp is paired with the unscaled Q by
   // the backward pass.
   constexpr bool kPre = kEpi != kEpiPlainLse;
-  // Four K/V buffers and one barrier per two tiles (the index-map windows
-  // keep two: their key-row table needs the LDS).  K buffers first, so that
-  // every K read (and every V read) is one base address plus an offset below
-  // 64 KB.
-  constexpr bool kPair = true;
+  // 256-query items: four K/V buffers in one array and one barrier per two
+  // tiles, K buffers first, so that every K read (and every V read) is one
+  // base address plus an offset below 64 KB.  128-query items (two
+  // workgroups per CU): two buffers and one barrier per tile, the buffer
+  // being read and the one being loaded in separate arrays -- the compiler
+  // then sees that the transposing V reads do not depend on the loads in
+  // flight (in one array it waits for all of them before such a read).
+  constexpr bool kPair = Rows::kQueries == kBM;
   constexpr int NBUF = kPair ? 4 : 2;
-  __shared__ __attribute__((aligned(1024))) uint16_t kv_lds[2 * NBUF][kBN * D];
-  uint16_t* const Ks0 = kv_lds[0];
-  uint16_t* const Ks1 = kv_lds[1];
-  uint16_t* const Vs0 = kv_lds[NBUF];
-  uint16_t* const Vs1 = kv_lds[NBUF + 1];
+  __shared__ __attribute__((aligned(1024))) uint16_t kv_lds[kPair ? 2 * NBUF : 2][kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t kv_lds1[kPair ? 1 : 2][kBN * D];
+  uint16_t *Ks0, *Ks1, *Vs0, *Vs1;
+  if constexpr (kPair) {
+    Ks0 = kv_lds[0];
+    Ks1 = kv_lds[1];
+    Vs0 = kv_lds[NBUF];
+    Vs1 = kv_lds[NBUF + 1];
+  } else {  // buffer 0 = kv_lds (K, V), buffer 1 = kv_lds1 (K, V)
+    Ks0 = kv_lds[0];
+    Vs0 = kv_lds[1];
+    Ks1 = kv_lds1[0];
+    Vs1 = kv_lds1[1];
+  }
   [[maybe_unused]] uint16_t* const Ks2 = kv_lds[kPair ? 2 : 0];
   [[maybe_unused]] uint16_t* const Ks3 = kv_lds[kPair ? 3 : 0];
   [[maybe_unused]] uint16_t* const Vs2 = kv_lds[kPair ? NBUF + 2 : 0];
@@ -700,12 +738,17 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave, 2) void attn_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave: scalar address arithmetic
   const int hh = lane >> 5, c = lane & 31;
   const int64_t hoff = (int64_t)w.head * D;
+  // The head's byte offset within a row, the scalar offset of the table
+  // loads.  Made uniform explicitly: the item decode divides on the VALU, and a
+  // value the compiler cannot prove uniform wraps every such load in a loop
+  // over the distinct values.
+  [[maybe_unused]] const int hoff_bytes = __builtin_amdgcn_readfirstlane((int)(hoff * 2));
   const int nfull = w.len / kBN;            // tiles without a group end inside
   const int ntiles = (w.len + kBN - 1) / kBN;
 
-  // Index-map windows: tabulate every key's token row once (up to kTabKeys).
-  __shared__ int32_t ktab[Rows::kTable ? kTabKeys : 1];
-  [[maybe_unused]] const bool use_tab = Rows::kTable && w.len <= kTabKeys;  // uniform per block
+  // Index-map windows: tabulate every key's token row once (up to tab_keys<Rows>()).
+  __shared__ int32_t ktab[tab_keys<Rows>()];
+  [[maybe_unused]] const bool use_tab = Rows::kTable && w.len <= tab_keys<Rows>();  // uniform per block
   [[maybe_unused]] bool use_tab32 = false;
   if constexpr (Rows::kTable) use_tab32 = use_tab && rows.tab_bytes != 0;
   if constexpr (Rows::kTable) {
@@ -743,7 +786,7 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave, 2) void attn_kernel(
     } else if (use_tab) {
       if (use_tab32)
         issue_tile_tab32<D, NW>(row_range_rsrc(K, 1, 0, (int)rows.tab_bytes),
-                                row_range_rsrc(V, 1, 0, (int)rows.tab_bytes), Kd, Vd, ktab, (int)(hoff * 2),
+                                row_range_rsrc(V, 1, 0, (int)rows.tab_bytes), Kd, Vd, ktab, hoff_bytes,
                                 t * kBN, wave, lane);
       else
         issue_tile_tab<D, NW>(K, V, Kd, Vd, ktab, w.len, row_stride, hoff, t * kBN, wave, lane);
@@ -794,7 +837,7 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave, 2) void attn_kernel(
     rs[b] = {0.f, 0.f};
   }
 
-  // Two buffers (index-map windows): tile t lives in buffer t % 2.  At the
+  // Two buffers (128-query items): tile t lives in buffer t % 2.  At the
   // top of each tile: wait for this wave's loads, barrier (all waves' loads
   // landed, tile t-1 fully consumed); the tile's step then starts the loads
   // of tile t+1 into the other buffer once its first K operand reads are
@@ -828,7 +871,7 @@ __global__ __launch_bounds__(waves_for<QB>() * kWave, 2) void attn_kernel(
         dma();
         tile_stats<D, QB, kMask, Rows::kVt>(Ks, t * kBN, w.len, qf, sc, mx, lsum, lane);
       } else {
-        tile_step<D, QB, kMask, Rows::kVt, kMode>(Ks, Vs, t * kBN, w.len, qf, o, rs, scale_log2, lane, dma);
+        tile_step<D, QB, kMask, Rows::kVt, kMode, !kPair>(Ks, Vs, t * kBN, w.len, qf, o, rs, scale_log2, lane, dma);
       }
     };
     using F = std::false_type;
@@ -1126,7 +1169,7 @@ int launch_attn(const void* Q, const void* K, const void* V, void* O, int64_t ro
   const int64_t run = (int64_t)kNumXcd * kXcdRun;
   const int64_t grid = ceil_div(items_bound, run) * run;
   if (grid > 0x7fffffff) return MOGA_ERR_SHAPE;
-  attn_kernel<D, kQB, Rows, kEpi><<<dim3((unsigned)grid), waves_for<kQB>() * kWave, 0, st>>>(
+  attn_kernel<D, kQB, Rows, kEpi><<<dim3((unsigned)grid), waves_for<Rows, kQB>() * kWave, 0, st>>>(
       static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V),
       static_cast<uint16_t*>(O), row_stride, scale * 1.4426950408889634f, epi, rows);
   MOGA_LAUNCH_CHECK();
@@ -1172,7 +1215,7 @@ extern "C" int moga_stga_attention(const void* Q, const void* K, const void* V, 
   if (N >= (int64_t(1) << 31)) return MOGA_ERR_SHAPE;
   if (gsize > (int64_t(1) << 20) || !valid_head_dims(H, D)) return MOGA_ERR_UNSUPPORTED;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
-  const int tpg = (int)ceil_div(gsize, kBM);
+  const int tpg = (int)ceil_div(gsize, StgaRows::kQueries);
   const int64_t items = (N / gsize) * H * tpg;
   if (items > 0x7fffffff) return MOGA_ERR_SHAPE;
   StgaRows rows{Hs, Ws, win_t, tile_h, tile_w, Hs / tile_h, Ws / tile_w, tpg, H, (int)items, table_bytes(N, H, D),
@@ -1278,7 +1321,7 @@ extern "C" int moga_stga_shot_attention(const void* Q, const void* K, const void
   if (!ws || ws_bytes < need) return MOGA_ERR_WORKSPACE;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
   const int max_windows = (int)(ceil_div(T, win_t) + n_shots);
-  const int tpg = (int)ceil_div((int64_t)win_t * area, kBM);
+  const int tpg = (int)ceil_div((int64_t)win_t * area, ShotRows::kQueries);
   const int ntx = Ws / tile_w, nspatial = (Hs / tile_h) * ntx;
   const int64_t items = (int64_t)max_windows * nspatial * H * tpg;
   if (items > 0x7fffffff) return MOGA_ERR_SHAPE;
