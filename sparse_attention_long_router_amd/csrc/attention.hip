@@ -1019,7 +1019,10 @@ __global__ __launch_bounds__((waves_for<Rows, QB>() * kWave), 2) void attn_kerne
     run(std::integral_constant<int, kPre ? kExpSub : kExpFma>{});
   }
 
-  // ---- normalise and store: reg r of block db is channel 32*db + 8*(r/4) + 4*hh + r%4
+  // ---- normalise and store: reg r of block db is channel 32*db + 8*(r/4) + 4*hh + r%4.
+  // 16-byte stores where registers allow; the pair-mode kernels that read V in
+  // row layout sit at the register limit and keep 8-byte ones.
+  constexpr bool kWideStore = Rows::kVt || !kPair;
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
     const float lsum = halves_sum(rs[b].l);
@@ -1043,32 +1046,71 @@ __global__ __launch_bounds__((waves_for<Rows, QB>() * kWave), 2) void attn_kerne
       keep = epi.beta;
     }
     uint16_t* op = O + orow * row_stride + hoff;
-    // STGA with beta != 0 (a branch summed onto another): every old value of
-    // the row is loaded before any is used, so the row costs one memory
-    // latency rather than one per 8-byte piece
-    u32x2 prev[DBLK][4];
     const bool acc = kEpi != kEpiPlain && keep != 0.f;  // uniform
-    if (kEpi == kEpiScaled && acc) {
+    if constexpr (kWideStore) {
+      // The lane halves hold alternating 4-channel pieces of a row; one
+      // v_permlane32_swap per value pairs them up so that every lane stores 8
+      // consecutive channels (16 bytes): half 0 channels 16m..16m+7 and half 1
+      // channels 16m+8..16m+15 of each 16-channel run m.  An accumulating
+      // epilogue loads the old values the same way, all of a row's before any
+      // is used (one memory latency per row).
+      u32x4 prev[DBLK][2];
+      if (acc) {
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+          for (int m = 0; m < 2; ++m) prev[db][m] = *reinterpret_cast<const u32x4*>(op + 32 * db + 16 * m + 8 * hh);
+      }
 #pragma unroll
       for (int db = 0; db < DBLK; ++db)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) prev[db][q4] = *reinterpret_cast<const u32x2*>(op + 32 * db + 8 * q4 + 4 * hh);
-    }
+        for (int m = 0; m < 2; ++m) {
+          float v[8];
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db)
+          for (int i = 0; i < 4; ++i) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(o[b][db][8 * m + i] * scale),
+                                                             __float_as_uint(o[b][db][8 * m + 4 + i] * scale),
+                                                             false, false);
+            v[i] = __uint_as_float(sw[0]);
+            v[4 + i] = __uint_as_float(sw[1]);
+          }
+          if (acc) {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = 32 * db + 8 * q4 + 4 * hh;
-        float v0 = o[b][db][4 * q4] * scale, v1 = o[b][db][4 * q4 + 1] * scale;
-        float v2 = o[b][db][4 * q4 + 2] * scale, v3 = o[b][db][4 * q4 + 3] * scale;
-        if (acc) {
-          const u32x2 old = kEpi == kEpiScaled ? prev[db][q4] : *reinterpret_cast<const u32x2*>(op + d0);
-          v0 += keep * bf16_lo(old[0]); v1 += keep * bf16_hi(old[0]);
-          v2 += keep * bf16_lo(old[1]); v3 += keep * bf16_hi(old[1]);
+            for (int k = 0; k < 4; ++k) {
+              v[2 * k] += keep * bf16_lo(prev[db][m][k]);
+              v[2 * k + 1] += keep * bf16_hi(prev[db][m][k]);
+            }
+          }
+          const u32x4 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                            pack_bf16x2(v[6], v[7])};
+          *reinterpret_cast<u32x4*>(op + 32 * db + 16 * m + 8 * hh) = pk;
         }
-        const u32x2 pk = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-        *reinterpret_cast<u32x2*>(op + d0) = pk;
+    } else {
+      // 8 bytes per lane and store; STGA with beta != 0 (a branch summed onto
+      // another) loads every old value of the row before any is used
+      u32x2 prev[DBLK][4];
+      if (kEpi == kEpiScaled && acc) {
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) prev[db][q4] = *reinterpret_cast<const u32x2*>(op + 32 * db + 8 * q4 + 4 * hh);
       }
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d0 = 32 * db + 8 * q4 + 4 * hh;
+          float v0 = o[b][db][4 * q4] * scale, v1 = o[b][db][4 * q4 + 1] * scale;
+          float v2 = o[b][db][4 * q4 + 2] * scale, v3 = o[b][db][4 * q4 + 3] * scale;
+          if (acc) {
+            const u32x2 old = kEpi == kEpiScaled ? prev[db][q4] : *reinterpret_cast<const u32x2*>(op + d0);
+            v0 += keep * bf16_lo(old[0]); v1 += keep * bf16_hi(old[0]);
+            v2 += keep * bf16_lo(old[1]); v3 += keep * bf16_hi(old[1]);
+          }
+          const u32x2 pk = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+          *reinterpret_cast<u32x2*>(op + d0) = pk;
+        }
+    }
   }
 }
 
