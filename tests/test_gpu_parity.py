@@ -287,6 +287,8 @@ def test_unpermute_accumulate(moga):
     (4, 30, 52, 2, 30, 26, 1, 128, 0.5, 0.5),  # Wan-like frames, groups of 1560
     (3, 8, 8, 1, 8, 8, 2, 64, 1.0, 1.0),
     (6, 30, 52, 6, 30, 52, 1, 64, 1.0, 0.0),     # 9,360-key window: past the key-row table
+    (5, 24, 32, 5, 24, 32, 2, 128, 1.0, 0.0),    # 3,840 keys: a full key-row table, 30 whole 128-query items
+    (5, 30, 26, 5, 30, 26, 1, 64, 1.0, 1.0),     # 3,900 keys: just past the table
 ])
 def test_stga(moga, T, Hs, Ws, win_t, th, tw, H, D, alpha, beta):
     N = T * Hs * Ws
@@ -360,17 +362,27 @@ def test_full_size_sampled(moga, name, path, seed):
     np.testing.assert_array_equal(fwd.cu_seqlens.cpu().numpy(), cu_ref)
     assert int(fwd.max_seqlen.item()) == mx_ref
 
-    rows = sample_rows(g_ref, wl.M, per_group=6, seed=wl.seed)
+    # the headline configuration gets a denser sample (about 1,000 rows)
+    rows = sample_rows(g_ref, wl.M, per_group=64 if name == "clip30s_122f" else 6, seed=wl.seed)
     # plus the queries on both sides of the first 32-query wave and 256-query
     # work-item boundaries of every group (permuted positions 31/32, 255/256)
     edges = [perm_ref[cu_ref[i] + j] for i in range(wl.M) for j in (31, 32, 255, 256)
              if cu_ref[i] + j < cu_ref[i + 1]]
+    if wl.stga is not None:
+        s = wl.stga
+        ids = oracle.stga_group_ids(s["T"], s["Hs"], s["Ws"], s["win_t"], s["tile_h"], s["tile_w"])
+        # the STGA windows are cut into 128-query work items: in the first and
+        # last window, the queries on both sides of the first item boundary
+        # and of the last (partial) item, in the window's own token order
+        for win in (0, int(ids.max())):
+            members = np.nonzero(ids == win)[0]
+            b = members.size // 128 * 128
+            edges += [int(members[j]) for j in sorted({0, 127, 128, b - 1, b, members.size - 1})
+                      if 0 <= j < members.size]
     rows = np.unique(np.concatenate([rows, np.asarray(edges, dtype=np.int64)]))
     Qn, Kn, Vn = _np(Q), _np(K), _np(V)
     want = oracle.moga_output_rows(Xn, Wn, Qn, Kn, Vn, wl.M, rows, routed=(g_ref, gate_ref))
     if wl.stga is not None:
-        s = wl.stga
-        ids = oracle.stga_group_ids(s["T"], s["Hs"], s["Ws"], s["win_t"], s["tile_h"], s["tile_w"])
         want = want + oracle.stga_attention_rows(Qn, Kn, Vn, ids, 1 / math.sqrt(wl.D), rows)
     got = _np(O[torch.from_numpy(rows).to(DEV)])
     e = assert_output_close(got, want, f"{name} sampled O")
