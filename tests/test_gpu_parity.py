@@ -289,6 +289,7 @@ def test_unpermute_accumulate(moga):
     (6, 30, 52, 6, 30, 52, 1, 64, 1.0, 0.0),     # 9,360-key window: past the key-row table
     (5, 24, 32, 5, 24, 32, 2, 128, 1.0, 0.0),    # 3,840 keys: a full key-row table, 30 whole 128-query items
     (5, 30, 26, 5, 30, 26, 1, 64, 1.0, 1.0),     # 3,900 keys: just past the table
+    (3, 30, 52, 3, 30, 26, 2, 128, 1.0, 1.0),    # the long-video windows (2,340 keys, a 36-query last item), accumulating
 ])
 def test_stga(moga, T, Hs, Ws, win_t, th, tw, H, D, alpha, beta):
     N = T * Hs * Ws
@@ -301,6 +302,18 @@ def test_stga(moga, T, Hs, Ws, win_t, th, tw, H, D, alpha, beta):
     ref = oracle.stga_attention(_np(Q), _np(K), _np(V), T, Hs, Ws, win_t, th, tw, 1 / math.sqrt(D),
                                 alpha=alpha, beta=beta, O_prev=_np(V))
     assert_output_close(_np(out), ref, "STGA")
+
+
+def test_stga_deterministic(moga):
+    """Every output row of an STGA window is written by one work item, so two
+    calls on the same inputs agree bit for bit."""
+    T, Hs, Ws = 3, 30, 52
+    inp = _inputs("tiny", N=T * Hs * Ws, H=2, D=128, M=2)
+    Q, K, V = inp["Q"], inp["K"], inp["V"]
+    a = moga.moga_stga_attention(Q, K, V, T, Hs, Ws, 3, 30, 26)
+    b = moga.moga_stga_attention(Q, K, V, T, Hs, Ws, 3, 30, 26)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
 
 
 @pytest.mark.parametrize("T,Hs,Ws,shots,win_t,th,tw,aug,H,D,alpha,beta", [
