@@ -67,11 +67,13 @@ constexpr int kBN = 64;                             // keys per LDS tile
 // this reads 6.0 GB from HBM per launch against 10.5 GB with runs of 8, in
 // the same time.
 constexpr int kXcdRun = 32;
-// Key-row table entries of an index-map window (Rows::kTabKeys): 4,096
-// (16 KB of LDS beside the four K/V buffers) for the shot-aware windows, which
-// reach (win_t + 2 augment) frames of a tile; 3,840 for the static windows
-// (2,340 keys in the long-video setting), whose two workgroups per CU share
-// the LDS.  Larger windows evaluate the map per load.
+// Key-row table entries of an index-map window (Rows::kTabKeys), sized so
+// that the table and two K/V buffers (64 KB) fit in half of a CU's 160 KB of
+// LDS and two workgroups share a CU: 4,096 (16 KB) for the shot-aware
+// windows, which reach (win_t + 2 augment) frames of a tile; 3,840 for the
+// static windows (2,340 keys in the long-video setting; the full 4,096 with
+// the reduction below measured 2.5% slower there).  Larger windows evaluate the
+// map per load.
 template <class Rows>
 constexpr int tab_keys() {
   if constexpr (Rows::kTable)
@@ -234,7 +236,7 @@ struct ShotWindow {
 // Items: window-major, then spatial tile, head and query tile, so the query
 // tiles sharing one key set are consecutive (and land on one XCD).
 struct ShotRows {
-  static constexpr int kQueries = kBM;
+  static constexpr int kQueries = 128;  // as StgaRows: two workgroups per CU
   static constexpr int kTabKeys = 4096;
   static constexpr bool kIndirect = false;
   static constexpr bool kContiguous = false;
@@ -998,7 +1000,23 @@ __global__ __launch_bounds__((waves_for<Rows, QB>() * kWave), 2) void attn_kerne
         for (int r = 0; r < 16; ++r) over |= !(__builtin_fabsf(o[b][db][r]) <= 3.402823466e38f);
     }
   }
-  if (__syncthreads_or(over)) {
+  // Whether any wave must recompute.  The 128-query items with a 4,096-entry
+  // key table reduce through the idle K/V buffer instead of __syncthreads_or,
+  // whose 256 bytes of LDS would keep their two workgroups off one CU.
+  constexpr bool kLdsTight = !kPair && 2 * 2 * kBN * D * 2 + tab_keys<Rows>() * 4 + 256 > 81920;
+  bool any_over;
+  if constexpr (!kLdsTight) {
+    any_over = __syncthreads_or(over);
+  } else {
+    __syncthreads();  // every wave is past its last read of the K/V buffers
+    int* const flags = reinterpret_cast<int*>(kv_lds[0]);
+    if (lane == 0) flags[wave] = __builtin_amdgcn_ballot_w64(over) != 0;
+    __syncthreads();
+    any_over = false;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) any_over |= flags[i] != 0;
+  }
+  if (any_over) {
     __syncthreads();
     issue_first();
     run(std::integral_constant<int, kStats>{});
