@@ -67,6 +67,9 @@ constexpr int kBN = 64;                             // keys per LDS tile
 // this reads 6.0 GB from HBM per launch against 10.5 GB with runs of 8, in
 // the same time.
 constexpr int kXcdRun = 32;
+// LDS of one CU (gfx950), and the bytes __syncthreads_or reserves for its reduction.
+constexpr int kCuLds = 160 * 1024;
+constexpr int kSyncOrLds = 256;
 // Key-row table entries of an index-map window (Rows::kTabKeys), sized so
 // that the table and two K/V buffers (64 KB) fit in half of a CU's 160 KB of
 // LDS and two workgroups share a CU: 4,096 (16 KB) for the shot-aware
@@ -1003,7 +1006,8 @@ __global__ __launch_bounds__((waves_for<Rows, QB>() * kWave), 2) void attn_kerne
   // Whether any wave must recompute.  The 128-query items with a 4,096-entry
   // key table reduce through the idle K/V buffer instead of __syncthreads_or,
   // whose 256 bytes of LDS would keep their two workgroups off one CU.
-  constexpr bool kLdsTight = !kPair && 2 * 2 * kBN * D * 2 + tab_keys<Rows>() * 4 + 256 > 81920;
+  constexpr bool kLdsTight =
+      !kPair && 2 * 2 * kBN * D * 2 + tab_keys<Rows>() * 4 + kSyncOrLds > kCuLds / 2;
   bool any_over;
   if constexpr (!kLdsTight) {
     any_over = __syncthreads_or(over);
