@@ -50,6 +50,8 @@ def make_parser():
                     choices=["fused_vtq", "fused_vt", "fused_epilogue", "gather_on_load", "separate"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass timing")
+    ap.add_argument("--no-staged-backward", action="store_true",
+                    help="time the attention backward with the minimum workspace only (dS not kept)")
     ap.add_argument("--cpu-rows", type=int, default=2000, help="sampled query rows per group for the oracle")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of MIB MiB (reference for HBM byte counters)")
@@ -175,40 +177,65 @@ def cpu_baseline(inp, wl, counts, rows_per_group):
     }
 
 
-def backward_timing(moga, wl, X, Wr, Q, K, V, flops_fwd, steps):
+def backward_timing(moga, wl, X, Wr, Q, K, V, flops_fwd, steps, staged=True):
     """The training backward of the MoGA layer (unpermute, attention and
     router backward) on the same inputs, after a training forward.  The
     attention's algorithmic work is 2.5x the forward's (five n^2 D products
-    per group and head: S, dP, dV, dQ, dK)."""
+    per group and head: S, dP, dV, dQ, dK).  With `staged`, the attention
+    backward gets the workspace that keeps dS (five products computed instead
+    of seven) when it fits in free device memory with 8 GiB to spare; the
+    minimum-workspace form is timed too and reported under "unstaged"."""
     import torch
 
     tr = moga.MogaTraining(wl.N, wl.d_model, wl.H, wl.D, wl.M, X.device)
     g = torch.Generator(device=X.device).manual_seed(wl.seed)
     dO = torch.randn(Q.shape, generator=g, device=X.device).bfloat16()
     tr.forward(X, Wr, Q, K, V)
-    tr.backward(dO)
-    torch.cuda.synchronize()
+    ws_min = tr.ws_bwd
+    ws_staged, ds_bytes = None, moga.moga_attention_backward_staged_bytes(tr.cu_seqlens, wl.H)
+    if staged and ds_bytes + (8 << 30) <= torch.cuda.mem_get_info()[0]:
+        ws_staged = torch.empty(ds_bytes, dtype=torch.uint8, device=X.device)
     stream = torch.cuda.current_stream()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-    for e in evs:
-        e[0].record(stream)
-        moga.moga_unpermute_backward(dO, tr.Op, tr.perm, tr.gate, tr.dOp, tr.delta, tr.dgate)
-        e[1].record(stream)
-        moga.moga_group_attention_backward(tr.Qp, tr.Kp, tr.Vp, tr.dOp, tr.lse, tr.delta, tr.cu_seqlens, tr.perm, 0.0,
-                                           tr.dQ, tr.dK, tr.dV, tr.ws_bwd)
-        e[2].record(stream)
-        moga.moga_route_backward(X, Wr, tr.group_id, tr.dgate, None, tr.dX, tr.dWr, tr.dbias, tr.ws_rbwd)
-        e[3].record(stream)
-    torch.cuda.synchronize()
-    names = ["unpermute_backward", "group_attention_backward", "route_backward"]
-    ms = {n: sum(e[k].elapsed_time(e[k + 1]) for e in evs) / steps for k, n in enumerate(names)}
+
+    def run(ws):
+        tr.ws_bwd = ws
+        tr.backward(dO)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        for e in evs:
+            e[0].record(stream)
+            moga.moga_unpermute_backward(dO, tr.Op, tr.perm, tr.gate, tr.dOp, tr.delta, tr.dgate)
+            e[1].record(stream)
+            moga.moga_group_attention_backward(tr.Qp, tr.Kp, tr.Vp, tr.dOp, tr.lse, tr.delta, tr.cu_seqlens, tr.perm,
+                                               0.0, tr.dQ, tr.dK, tr.dV, ws)
+            e[2].record(stream)
+            moga.moga_route_backward(X, Wr, tr.group_id, tr.dgate, None, tr.dX, tr.dWr, tr.dbias, tr.ws_rbwd)
+            e[3].record(stream)
+        torch.cuda.synchronize()
+        names = ["unpermute_backward", "group_attention_backward", "route_backward"]
+        return {n: sum(e[k].elapsed_time(e[k + 1]) for e in evs) / steps for k, n in enumerate(names)}
+
+    def frac(attn_ms):
+        return 2.5 * flops_fwd / (attn_ms * 1e-3) / 1e12
+
+    ms_min = run(ws_min)
+    ms = ms_min
+    used = False
+    if ws_staged is not None:
+        ms = run(ws_staged)
+        used = moga.moga_attention_backward_staged(ws_staged)
     total = sum(ms.values())
     attn = ms["group_attention_backward"]
-    del tr
+    del tr, ws_staged
     return {"ms": round(total, 4), "breakdown_ms": {k: round(v, 4) for k, v in ms.items()}, "steps": steps,
-            "attention_tflops": round(2.5 * flops_fwd / (attn * 1e-3) / 1e12, 2),
-            "attention_mfma_frac": round(2.5 * flops_fwd / (attn * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "attention_tflops": round(frac(attn), 2),
+            "attention_mfma_frac": round(frac(attn) / PEAK_BF16_TFLOPS, 4),
             "flops_per_launch": 2.5 * flops_fwd,
+            "ds_staged": used, "ds_workspace_bytes": ds_bytes,
+            "unstaged": {"group_attention_backward_ms": round(ms_min["group_attention_backward"], 4),
+                         "attention_tflops": round(frac(ms_min["group_attention_backward"]), 2),
+                         "attention_mfma_frac": round(frac(ms_min["group_attention_backward"]) / PEAK_BF16_TFLOPS,
+                                                      4)},
             "unpermute_backward_gbs": round(wl.N * (6 * wl.H * wl.D + 4 * wl.H + 12) / (ms["unpermute_backward"] * 1e-3)
                                             / 1e9, 1)}
 
@@ -357,7 +384,8 @@ def main():
     }
     if not args.no_backward:
         del fwd  # free the forward buffers before the training ones
-        out["backward"] = backward_timing(moga, wl, X, Wr, Q, K, V, flops_moga, steps=max(2, args.steps // 4))
+        out["backward"] = backward_timing(moga, wl, X, Wr, Q, K, V, flops_moga, steps=max(2, args.steps // 4),
+                                          staged=not args.no_staged_backward)
     hbm = {"route": wl.N * (2 * wl.d_model + 8) + 2 * wl.M * wl.d_model}  # algorithmic bytes per launch
     # sort + gather; the sort alone is latency-bound (reported in ms only)
     if args.path == "fused_vtq":  # K and V gathered, Q read through perm by the attention

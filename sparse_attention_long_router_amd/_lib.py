@@ -56,6 +56,7 @@ SIGNATURES = {
     "moga_unpermute_backward": (_c.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),
     "moga_group_attention_backward": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
                                                  _f32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moga_attention_backward_staged_bytes": (_sz, [_vp, _i32, _i32]),
     "moga_route_backward": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moga_workspace_bytes": (_sz, [_i32, _i64, _i32, _i32, _i32]),
     "moga_strerror": (_c.c_char_p, [_i32]),
@@ -65,7 +66,7 @@ SIGNATURES = {
 
 BUILD_HINT = "run `python sparse_attention_long_router_amd/build.py`"
 # moga_version() of the sources this binding matches (csrc/api.hip)
-EXPECTED_VERSION = 400
+EXPECTED_VERSION = 410
 
 
 def _load():

@@ -8,6 +8,8 @@ Python.
 
 from __future__ import annotations
 
+import ctypes
+
 import torch
 
 from . import _lib
@@ -549,6 +551,30 @@ def moga_group_attention_backward(Qp, Kp, Vp, dOp, lse, delta, cu_seqlens, perm,
     return dQ, dK, dV
 
 
+def moga_attention_backward_staged_bytes(cu_seqlens, H: int) -> int:
+    """Workspace of moga_group_attention_backward that keeps dS for these
+    groups (cu_seqlens int32 [M + 1], copied to the host if on the device)."""
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor")
+    host = cu_seqlens.detach().to("cpu").contiguous()
+    M = host.shape[0] - 1
+    n = int(_lib.LIB.moga_attention_backward_staged_bytes(ctypes.c_void_p(host.data_ptr()), M, int(H)))
+    if n == 0:
+        raise ValueError("moga_attention_backward_staged_bytes: invalid cu_seqlens or H")
+    return n
+
+
+STAGED_FLAG_OFFSET = 2560  # MOGA_BWD_STAGED_FLAG_OFFSET in include/moga.h
+
+
+def moga_attention_backward_staged(ws) -> bool:
+    """Whether the last moga_group_attention_backward on this workspace kept
+    dS (reads the flag the call leaves in ws; synchronises)."""
+    if ws.numel() * ws.element_size() <= 4096:
+        return False
+    return bool(ws.view(torch.uint8)[STAGED_FLAG_OFFSET:STAGED_FLAG_OFFSET + 4].view(torch.int32).item())
+
+
 def moga_route_backward(X, Wr, group_id, dgate, bias=None, dX=None, dWr=None, dbias=None, ws=None):
     """Router gradients (dX float32 [N, d_model], dWr float32 [M, d_model],
     dbias float32 [M]) from dgate."""
@@ -579,9 +605,14 @@ class MogaTraining:
     keeps what the backward needs; ``backward(dO)`` runs the unpermute,
     attention and router backward and returns the gradients of sum(O * dO)
     w.r.t. Q, K, V (bf16, original order), the router's share of dX, dWr and
-    dbias (float32), plus dgate.  Buffers are allocated once."""
+    dbias (float32), plus dgate.  Buffers are allocated once.
 
-    def __init__(self, N, d_model, H, D, M, device):
+    ``ds_bytes`` > 0 gives the attention backward a workspace of that many
+    bytes, in which it keeps dS whenever the groups of the call fit (see
+    ``moga_attention_backward_staged_bytes``): five matrix products instead
+    of seven, for sum_g H * n_g^2 * 2 bytes of device memory."""
+
+    def __init__(self, N, d_model, H, D, M, device, ds_bytes=0):
         self.N, self.d_model, self.H, self.D, self.M = N, d_model, H, D, M
         e = lambda *s, dt=BF16: torch.empty(*s, dtype=dt, device=device)  # noqa: E731
         self.group_id, self.gate = e(N, dt=torch.int32), e(N, dt=F32)
@@ -590,7 +621,8 @@ class MogaTraining:
         self.perm, self.cu_seqlens, self.max_seqlen = e(N, dt=torch.int32), e(M + 1, dt=torch.int32), e(1, dt=torch.int32)
         self.ws_perm = e(max(moga_workspace_bytes(MOGA_OP_PERMUTE, N, M, H, D), 1), dt=torch.uint8)
         self.ws_attn = e(max(moga_workspace_bytes(MOGA_OP_GROUP_ATTENTION, N, M, H, D), 1), dt=torch.uint8)
-        self.ws_bwd = e(max(moga_workspace_bytes(MOGA_OP_ATTENTION_BACKWARD, N, M, H, D), 1), dt=torch.uint8)
+        self.ws_bwd = e(max(moga_workspace_bytes(MOGA_OP_ATTENTION_BACKWARD, N, M, H, D), int(ds_bytes), 1),
+                        dt=torch.uint8)
         self.ws_rbwd = e(max(moga_workspace_bytes(MOGA_OP_ROUTE_BACKWARD, N, M, 1, d_model), 1), dt=torch.uint8)
         self.dOp, self.delta, self.dgate = e(N, H, D), e(H, N, dt=F32), e(N, dt=F32)
         self.dQ, self.dK, self.dV = (e(N, H, D) for _ in range(3))

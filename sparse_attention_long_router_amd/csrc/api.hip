@@ -40,4 +40,4 @@ extern "C" const char* moga_strerror(int32_t status) {
 // 0.3.0: transposed-V gather and attention (moga_permute_vt, moga_group_attention_unpermute_vt)
 // 0.3.1: queries read through perm (moga_group_attention_unpermute_vtq; moga_permute_vt without Q)
 // 0.4.0: moga_route and moga_stga_attention take (ws, ws_bytes) like the other steps
-extern "C" int32_t moga_version(void) { return 400; }
+extern "C" int32_t moga_version(void) { return 410; }

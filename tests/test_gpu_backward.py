@@ -42,14 +42,26 @@ def _case(name, seed=None, bias=False, **over):
     return X, Wr, Q, K, V, dO, b
 
 
-def _check(moga, X, Wr, Q, K, V, dO, bias=None, label=""):
+def _stage(moga, tr, extra):
+    """Give tr's attention backward the workspace that keeps dS for its
+    groups, plus `extra` bytes (negative: too small by that much)."""
+    need = moga.moga_attention_backward_staged_bytes(tr.cu_seqlens, tr.H)
+    tr.ws_bwd = torch.empty(need + extra, dtype=torch.uint8, device=DEV)
+    return need
+
+
+def _check(moga, X, Wr, Q, K, V, dO, bias=None, label="", staged=None):
     N, H, D = Q.shape
     M, d = Wr.shape
-    print(f"[backward] {label} N={N} H={H} D={D} M={M} d={d}", flush=True)
+    print(f"[backward] {label} N={N} H={H} D={D} M={M} d={d} staged={staged}", flush=True)
     tr = moga.MogaTraining(N, d, H, D, M, DEV)
     tr.forward(X, Wr, Q, K, V, bias)
+    if staged is not None:
+        _stage(moga, tr, staged)
     grads = tr.backward(dO)
     torch.cuda.synchronize()
+    if staged is not None:
+        assert moga.moga_attention_backward_staged(tr.ws_bwd) == (staged >= 0)
     ref = oracle.moga_backward(_np(X), _np(Wr), _np(Q), _np(K), _np(V), M, _np(dO),
                                bias=None if bias is None else bias.cpu().numpy())
     np.testing.assert_array_equal(tr.group_id.cpu().numpy(), ref["group_id"])
@@ -116,8 +128,59 @@ def test_backward_deterministic(moga):
         assert torch.equal(a[k], b[k]), k
 
 
-@pytest.mark.parametrize("name", ["wan13b_21f", "clip30s_122f"])
-def test_backward_full_size(moga, name):
+def _unstaged(moga, tr):
+    """The attention backward of tr's saved state with the minimum workspace."""
+    return moga.moga_group_attention_backward(tr.Qp, tr.Kp, tr.Vp, tr.dOp, tr.lse, tr.delta, tr.cu_seqlens,
+                                              tr.perm, 0.0)
+
+
+@pytest.mark.parametrize("N,H,D,M,d", [
+    (3001, 2, 128, 5, 256),   # ragged groups: partial key and query blocks, odd block counts
+    (777, 3, 64, 3, 128),
+    (1, 2, 128, 4, 128),      # one token: one block of one query and one key, plus the zero padding block
+    (2000, 1, 64, 64, 128),   # many (and empty) groups
+    (9000, 2, 128, 3, 128),   # groups of thousands: many 64-key tiles per dQ item
+])
+def test_backward_staged(moga, N, H, D, M, d):
+    """dS kept in the workspace: gradients against the oracle; dK and dV
+    bitwise those of the minimum-workspace call (same kernel arithmetic), dQ
+    within float32 rounding of it."""
+    X, Wr, Q, K, V, dO, _ = _case("wan13b_21f", seed=81 + N, N=N, H=H, D=D, M=M, d_model=d)
+    tr, grads = _check(moga, X, Wr, Q, K, V, dO, label=f"staged {N, H, D, M, d}", staged=0)
+    dQ, dK, dV = _unstaged(moga, tr)
+    torch.cuda.synchronize()
+    assert torch.equal(dK, grads["dK"]) and torch.equal(dV, grads["dV"])
+    diff = (dQ.float() - grads["dQ"].float()).norm() / max(dQ.float().norm().item(), 1e-30)
+    print(f"[backward] staged vs unstaged dQ rel_fro {diff.item():.2e} "
+          f"(bitwise {torch.equal(dQ, grads['dQ'])})", flush=True)
+    assert diff.item() <= 1e-2
+
+
+def test_backward_staged_too_small(moga):
+    """A workspace one byte short of the staged size: the device plan falls
+    back to the unstaged form, bitwise the minimum-workspace result."""
+    X, Wr, Q, K, V, dO, _ = _case("wan13b_21f", seed=83, N=3001, H=2, D=128, M=5, d_model=256)
+    tr, grads = _check(moga, X, Wr, Q, K, V, dO, label="staged, one byte short", staged=-1)
+    dQ, dK, dV = _unstaged(moga, tr)
+    torch.cuda.synchronize()
+    assert torch.equal(dQ, grads["dQ"]) and torch.equal(dK, grads["dK"]) and torch.equal(dV, grads["dV"])
+
+
+def test_backward_staged_deterministic(moga):
+    X, Wr, Q, K, V, dO, _ = _case("wan13b_21f", seed=84, N=4000, H=2, D=128, M=4, d_model=128)
+    tr = moga.MogaTraining(4000, 128, 2, 128, 4, DEV)
+    tr.forward(X, Wr, Q, K, V)
+    _stage(moga, tr, 4096)
+    a = {k: v.clone() for k, v in tr.backward(dO).items()}
+    b = tr.backward(dO)
+    torch.cuda.synchronize()
+    assert moga.moga_attention_backward_staged(tr.ws_bwd)
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("name,staged", [("wan13b_21f", False), ("clip30s_122f", False), ("clip30s_122f", True)])
+def test_backward_full_size(moga, name, staged):
     """Full-size training backward in the configuration the bench times:
     sampled rows of dQ, dgate and the router's dX against the oracle row by
     row, and two group invariants over every row: a group's dV sums to its
@@ -132,8 +195,11 @@ def test_backward_full_size(moga, name):
     dO = torch.randn(Q.shape, generator=g, device=DEV).bfloat16()
     tr = moga.MogaTraining(wl.N, wl.d_model, wl.H, wl.D, wl.M, DEV)
     tr.forward(X, Wr, Q, K, V)
+    if staged:
+        print(f"[backward] full size {name}: staged dS workspace {_stage(moga, tr, 0) / 2**30:.1f} GiB", flush=True)
     grads = tr.backward(dO)
     torch.cuda.synchronize()
+    assert moga.moga_attention_backward_staged(tr.ws_bwd) == staged
     Xn, Wn = _np(X), _np(Wr)
     g_ref, _, logits = oracle.route(Xn, Wn)
     np.testing.assert_array_equal(tr.group_id.cpu().numpy(), g_ref)
