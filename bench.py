@@ -182,9 +182,10 @@ def backward_timing(moga, wl, X, Wr, Q, K, V, flops_fwd, steps, staged=True):
     router backward) on the same inputs, after a training forward.  The
     attention's algorithmic work is 2.5x the forward's (five n^2 D products
     per group and head: S, dP, dV, dQ, dK).  With `staged`, the attention
-    backward gets the workspace that keeps dS (five products computed instead
-    of seven) when it fits in free device memory with 8 GiB to spare; the
-    minimum-workspace form is timed too and reported under "unstaged"."""
+    backward gets a workspace that keeps dS (five products computed instead
+    of seven) for every head, or for as many heads as free device memory
+    holds with 8 GiB to spare; the minimum-workspace form is timed too and
+    reported under "unstaged"."""
     import torch
 
     tr = moga.MogaTraining(wl.N, wl.d_model, wl.H, wl.D, wl.M, X.device)
@@ -193,8 +194,11 @@ def backward_timing(moga, wl, X, Wr, Q, K, V, flops_fwd, steps, staged=True):
     tr.forward(X, Wr, Q, K, V)
     ws_min = tr.ws_bwd
     ws_staged, ds_bytes = None, moga.moga_attention_backward_staged_bytes(tr.cu_seqlens, wl.H)
-    if staged and ds_bytes + (8 << 30) <= torch.cuda.mem_get_info()[0]:
-        ws_staged = torch.empty(ds_bytes, dtype=torch.uint8, device=X.device)
+    per_head = (ds_bytes - 4096) // wl.H
+    room = torch.cuda.mem_get_info()[0] - (8 << 30) - 4096
+    heads_fit = min(wl.H, max(room, 0) // max(per_head, 1))
+    if staged and heads_fit >= 1:
+        ws_staged = torch.empty(4096 + heads_fit * per_head, dtype=torch.uint8, device=X.device)
     stream = torch.cuda.current_stream()
 
     def run(ws):
@@ -220,18 +224,20 @@ def backward_timing(moga, wl, X, Wr, Q, K, V, flops_fwd, steps, staged=True):
 
     ms_min = run(ws_min)
     ms = ms_min
-    used = False
+    used = 0
     if ws_staged is not None:
         ms = run(ws_staged)
         used = moga.moga_attention_backward_staged(ws_staged)
     total = sum(ms.values())
     attn = ms["group_attention_backward"]
+    ws_staged_bytes = None if ws_staged is None else ws_staged.numel()
     del tr, ws_staged
     return {"ms": round(total, 4), "breakdown_ms": {k: round(v, 4) for k, v in ms.items()}, "steps": steps,
             "attention_tflops": round(frac(attn), 2),
             "attention_mfma_frac": round(frac(attn) / PEAK_BF16_TFLOPS, 4),
             "flops_per_launch": 2.5 * flops_fwd,
-            "ds_staged": used, "ds_workspace_bytes": ds_bytes,
+            "ds_staged_heads": used, "ds_bytes_all_heads": ds_bytes,
+            "ds_workspace_bytes": 0 if ws_staged_bytes is None else ws_staged_bytes,
             "unstaged": {"group_attention_backward_ms": round(ms_min["group_attention_backward"], 4),
                          "attention_tflops": round(frac(ms_min["group_attention_backward"]), 2),
                          "attention_mfma_frac": round(frac(ms_min["group_attention_backward"]) / PEAK_BF16_TFLOPS,

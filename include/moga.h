@@ -345,15 +345,16 @@ int moga_unpermute_backward(const void* dO, const void* Op, const int32_t* perm,
  *   written in ORIGINAL token order through perm (row perm[j] gets the
  *   gradient of permuted row j).  Deterministic (no atomics).
  *   ws: at least moga_workspace_bytes(MOGA_OP_ATTENTION_BACKWARD, N, M, H, D).
- *   A larger workspace, moga_attention_backward_staged_bytes() for this
- *   call's groups, lets the call keep dS in it (bf16, sum over groups of
- *   H * n_g^2 * 2 bytes) and form dQ from it: five matrix products per group
- *   and head instead of seven.  Whether the groups fit is decided on the
- *   device, from cu_seqlens; when they do not, the call computes dQ without
- *   dS, as with the minimum workspace.  After the call, the int32 at byte
- *   offset MOGA_BWD_STAGED_FLAG_OFFSET of ws reads 1 if dS was staged and 0
- *   otherwise (only written when ws_bytes > 4096).  dK and dV are bitwise the
- *   same either way; dQ agrees to the float32 rounding of the product order.
+ *   A larger workspace lets the call keep dS in it (bf16, about n_g^2 * 2
+ *   bytes per group and head) and form dQ from it: five matrix products per
+ *   group and head instead of seven.  moga_attention_backward_staged_bytes()
+ *   gives the size that holds every head of this call's groups; a smaller
+ *   one (above 4096 bytes) holds the first Hs heads that fit, and the others
+ *   are computed without dS, as with the minimum workspace.  Hs is decided on
+ *   the device, from cu_seqlens; after the call the int32 at byte offset
+ *   MOGA_BWD_STAGED_FLAG_OFFSET of ws reads Hs (written only when
+ *   ws_bytes > 4096).  dK and dV are bitwise the same either way; dQ agrees
+ *   to the float32 rounding of the product order.
  */
 #define MOGA_BWD_STAGED_FLAG_OFFSET 2560
 int moga_group_attention_backward(const void* Qp, const void* Kp, const void* Vp, const void* dOp,
@@ -364,9 +365,9 @@ int moga_group_attention_backward(const void* Qp, const void* Kp, const void* Vp
 
 /*
  * moga_attention_backward_staged_bytes -- workspace of
- *   moga_group_attention_backward that keeps dS for these groups: 4096 +
- *   sum over groups of H * ceil(n_g / 32) * (that rounded up to even) * 2048
- *   bytes.  cu_seqlens_host: HOST int32 [M + 1] (a copy of the device array).
+ *   moga_group_attention_backward that keeps dS of all H heads for these
+ *   groups: 4096 + H * sum over groups of ceil(n_g / 32) * (that rounded up
+ *   to even) * 2048 bytes (each head adds an equal share).  cu_seqlens_host: HOST int32 [M + 1] (a copy of the device array).
  *   0 for invalid arguments (M outside 1..64, H < 1, a negative group size or
  *   one above 2^24 tokens).  Host-only, no device call.
  */

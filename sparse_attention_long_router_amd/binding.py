@@ -567,12 +567,12 @@ def moga_attention_backward_staged_bytes(cu_seqlens, H: int) -> int:
 STAGED_FLAG_OFFSET = 2560  # MOGA_BWD_STAGED_FLAG_OFFSET in include/moga.h
 
 
-def moga_attention_backward_staged(ws) -> bool:
-    """Whether the last moga_group_attention_backward on this workspace kept
-    dS (reads the flag the call leaves in ws; synchronises)."""
+def moga_attention_backward_staged(ws) -> int:
+    """Heads whose dS the last moga_group_attention_backward on this
+    workspace kept (reads the count the call leaves in ws; synchronises)."""
     if ws.numel() * ws.element_size() <= 4096:
-        return False
-    return bool(ws.view(torch.uint8)[STAGED_FLAG_OFFSET:STAGED_FLAG_OFFSET + 4].view(torch.int32).item())
+        return 0
+    return int(ws.view(torch.uint8)[STAGED_FLAG_OFFSET:STAGED_FLAG_OFFSET + 4].view(torch.int32).item())
 
 
 def moga_route_backward(X, Wr, group_id, dgate, bias=None, dX=None, dWr=None, dbias=None, ws=None):
@@ -608,9 +608,10 @@ class MogaTraining:
     dbias (float32), plus dgate.  Buffers are allocated once.
 
     ``ds_bytes`` > 0 gives the attention backward a workspace of that many
-    bytes, in which it keeps dS whenever the groups of the call fit (see
+    bytes, in which it keeps dS for as many heads as fit (all of them with
     ``moga_attention_backward_staged_bytes``): five matrix products instead
-    of seven, for sum_g H * n_g^2 * 2 bytes of device memory."""
+    of seven for those heads, for about sum_g n_g^2 * 2 bytes of device
+    memory per head."""
 
     def __init__(self, N, d_model, H, D, M, device, ds_bytes=0):
         self.N, self.d_model, self.H, self.D, self.M = N, d_model, H, D, M

@@ -18,10 +18,11 @@
 //     and values stream through LDS as in the forward pass.  S^T = K Q^T and
 //     dP^T = V dA^T put one query per lane, and dQ^T += K^T dS^T.
 // With a workspace large enough for it (moga_group_attention_backward decides
-// on the device), dkdv_kernel also stores dS in bf16, which the dq kernel
-// rounds it to anyway, and dq_ds_kernel computes dQ = c dS K from it: five
-// products per group and head instead of seven (S and dP are not computed a
-// second time), for sum_g H * n_g^2 * 2 bytes of HBM.  The dS of group g,
+// on the device, head by head), dkdv_kernel also stores dS in bf16, which the
+// dq kernel rounds it to anyway, and dq_ds_kernel computes dQ = c dS K from
+// it: five products per group and head instead of seven (S and dP are not
+// computed a second time), for sum_g n_g^2 * 2 bytes of HBM per staged head.
+// The first Hs heads that fit are staged; dq_kernel takes the others.  The dS of group g,
 // head h is stored in blocks of 32 queries x 32 keys (2 KB): block (qb, kb)
 // at off[g] + ((h * nb + qb) * nbp + kb) * 2048 bytes, nb = ceil(n_g / 32),
 // nbp = nb rounded up to even (the padding block holds zeros).  A block is
@@ -70,11 +71,11 @@ constexpr int kCpolNt = 2;     // cache policy of the dS stores and loads: non-t
 // Where the staged dS of each group starts, and whether it fits the workspace.
 struct DsPlan {
   int64_t off[kMaxGroups];  // byte offset of group g's blocks in the dS area
-  int32_t use;              // 1: dkdv stores dS and dq_ds_kernel computes dQ from it
+  int32_t heads;            // heads 0 .. heads-1 are staged: dkdv stores their dS, dq_ds_kernel forms their dQ
 };
 constexpr size_t kDsPlanOffset = 2048;  // in the workspace, after the two schedules
 constexpr size_t kDsDataOffset = 4096;  // start of the dS area
-static_assert(kDsPlanOffset + offsetof(DsPlan, use) == MOGA_BWD_STAGED_FLAG_OFFSET, "flag offset in moga.h");
+static_assert(kDsPlanOffset + offsetof(DsPlan, heads) == MOGA_BWD_STAGED_FLAG_OFFSET, "flag offset in moga.h");
 static_assert(kDsPlanOffset + sizeof(DsPlan) <= kDsDataOffset, "plan fits before the dS area");
 
 // s_waitcnt for vector memory only: at most N of this wave's loads outstanding.
@@ -278,25 +279,19 @@ __device__ __forceinline__ bool decode(const AttnSchedule* sched, const int32_t*
 
 // ---------------------------------------------------------------------------
 // dK, dV: 4 waves x 32 keys, queries streamed in tiles of kTileQ (128)
-// kStage: also store dS where the plan says it fits.
+// kStage: the kernel may stage dS (the plan names the heads).
 // ---------------------------------------------------------------------------
+// One dkdv work item; kStage: this head's dS is staged (also stored).
 template <int D, bool kStage>
-__global__ __launch_bounds__(kDkvWaves * kWave) void dkdv_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+__device__ __forceinline__ void dkdv_item(
+    const Item& w, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dA, const float* __restrict__ lse, const float* __restrict__ delta,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ perm, const AttnSchedule* __restrict__ sched, int M,
-    int64_t N, int64_t row_stride, float scale, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
-    const DsPlan* __restrict__ plan, uint8_t* __restrict__ ds) {
+    const int32_t* __restrict__ perm, int64_t N, int64_t row_stride, float scale, uint16_t* __restrict__ dK,
+    uint16_t* __restrict__ dV, const DsPlan* __restrict__ plan, uint8_t* __restrict__ ds,
+    uint16_t (&Qs)[2][kTileQ * D], uint16_t (&As)[2][kTileQ * D], float (&Ls)[2][kTileQ], float (&Ds)[2][kTileQ]) {
   constexpr int DBLK = D / 32;
   constexpr int NW = kDkvWaves;
   constexpr int kTile = kTileQ;
-  __shared__ __attribute__((aligned(1024))) uint16_t Qs[2][kTile * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t As[2][kTile * D];
-  __shared__ __attribute__((aligned(256))) float Ls[2][kTile];
-  __shared__ __attribute__((aligned(256))) float Ds[2][kTile];
-
-  Item w;
-  if (!decode(sched, cu, M, kDkvBN, xcd_remap(blockIdx.x, kRun), w)) return;
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar descriptors, no waterfall
   const int64_t hoff = (int64_t)w.head * D;
@@ -344,14 +339,12 @@ __global__ __launch_bounds__(kDkvWaves * kWave) void dkdv_kernel(
   int ds_nb = 0;               // query blocks of the group (0: nothing staged)
   uint32_t ds_pitch = 0;       // bytes between query blocks of the column
   if constexpr (kStage) {
-    if (plan->use) {
-      const int nb = (w.len + 31) >> 5, nbp = (nb + 1) & ~1;
-      const int kblk = (w.t0 >> 5) + wave;  // uniform per wave
-      if (kblk < nbp) {
-        ds_col = ds + plan->off[w.g] + ((int64_t)w.head * nb * nbp + kblk) * kDsBlock;
-        ds_nb = nb;
-        ds_pitch = (uint32_t)nbp * kDsBlock;
-      }
+    const int nb = (w.len + 31) >> 5, nbp = (nb + 1) & ~1;
+    const int kblk = (w.t0 >> 5) + wave;  // uniform per wave
+    if (kblk < nbp) {
+      ds_col = ds + plan->off[w.g] + ((int64_t)w.head * nb * nbp + kblk) * kDsBlock;
+      ds_nb = nb;
+      ds_pitch = (uint32_t)nbp * kDsBlock;
     }
   }
 
@@ -426,6 +419,30 @@ __global__ __launch_bounds__(kDkvWaves * kWave) void dkdv_kernel(
   }
 }
 
+template <int D, bool kStage>
+__global__ __launch_bounds__(kDkvWaves * kWave) void dkdv_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dA, const float* __restrict__ lse, const float* __restrict__ delta,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ perm, const AttnSchedule* __restrict__ sched, int M,
+    int64_t N, int64_t row_stride, float scale, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
+    const DsPlan* __restrict__ plan, uint8_t* __restrict__ ds) {
+  __shared__ __attribute__((aligned(1024))) uint16_t Qs[2][kTileQ * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t As[2][kTileQ * D];
+  __shared__ __attribute__((aligned(256))) float Ls[2][kTileQ];
+  __shared__ __attribute__((aligned(256))) float Ds[2][kTileQ];
+
+  Item w;
+  if (!decode(sched, cu, M, kDkvBN, xcd_remap(blockIdx.x, kRun), w)) return;
+  if constexpr (kStage) {
+    // heads past the plan's count run the form without stores
+    if (w.head < plan->heads) {
+      dkdv_item<D, true>(w, Q, K, V, dA, lse, delta, perm, N, row_stride, scale, dK, dV, plan, ds, Qs, As, Ls, Ds);
+      return;
+    }
+  }
+  dkdv_item<D, false>(w, Q, K, V, dA, lse, delta, perm, N, row_stride, scale, dK, dV, plan, ds, Qs, As, Ls, Ds);
+}
+
 // ---------------------------------------------------------------------------
 // dQ: 8 waves x 32 queries, keys and values streamed in tiles of kTileK (128)
 // ---------------------------------------------------------------------------
@@ -441,9 +458,9 @@ __global__ __launch_bounds__(kDqWaves * kWave) void dq_kernel(
   __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][kTile * D];
   __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][kTile * D];
 
-  if (plan != nullptr && plan->use) return;  // dq_ds_kernel computes dQ from the staged dS
   Item w;
   if (!decode(sched, cu, M, kDqBM, xcd_remap(blockIdx.x, kRun), w)) return;
+  if (plan != nullptr && w.head < plan->heads) return;  // dq_ds_kernel forms this head's dQ from the staged dS
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t hoff = (int64_t)w.head * D;
@@ -539,9 +556,9 @@ __global__ __launch_bounds__(kDqWaves * kWave) void dq_ds_kernel(
   __shared__ __attribute__((aligned(1024))) uint16_t Sl0[NW * kSw];
   __shared__ __attribute__((aligned(1024))) uint16_t Sl1[NW * kSw];
 
-  if (!plan->use) return;  // dq_kernel computes dQ
   Item w;
   if (!decode(sched, cu, M, kDqBM, xcd_remap(blockIdx.x, kRun), w)) return;
+  if (w.head >= plan->heads) return;  // dq_kernel computes this head's dQ
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t hoff = (int64_t)w.head * D;
@@ -653,28 +670,31 @@ __global__ __launch_bounds__(kDqWaves * kWave) void dq_ds_kernel(
   }
 }
 
-// Staged-dS plan: per-group byte offsets (group index order) and whether the
-// total fits `capacity`.  One wave; a group's bytes saturate at 2^56 so that
-// the sum cannot overflow (such a total never fits).
+// Staged-dS plan: as many heads as the capacity holds (all of them, or the
+// first Hs), and per-group byte offsets of their blocks (group index order,
+// group g holding Hs * nb_g * nbp_g blocks).  One wave; a group's bytes per
+// head saturate at 2^50 so that the sum cannot overflow (such a group never
+// fits).
 __global__ __launch_bounds__(kWave) void ds_plan_kernel(const int32_t* __restrict__ cu, int M, int H,
                                                       int64_t capacity, DsPlan* __restrict__ plan) {
   const int g = threadIdx.x;
-  int64_t bytes = 0;
+  const int64_t cap = int64_t(1) << 50;
+  int64_t bytes = 0;  // per head
   if (g < M) {
     const int64_t n = (int64_t)cu[g + 1] - cu[g];
     const int64_t nb = (n + 31) >> 5, nbp = (nb + 1) & ~int64_t(1);
-    const int64_t cap = int64_t(1) << 56;
-    bytes = nb > (int64_t(1) << 19) ? cap : (int64_t)H * nb * nbp * kDsBlock;
-    bytes = bytes < cap ? bytes : cap;
+    bytes = nb > (int64_t(1) << 19) ? cap : nb * nbp * kDsBlock;
   }
   int64_t incl = bytes;
   for (int off = 1; off < kWave; off <<= 1) {
     const int64_t v = __shfl_up(incl, off);
     if (g >= off) incl += v;
   }
-  if (g < M) plan->off[g] = incl - bytes;
-  const int64_t total = __shfl(incl, M - 1);
-  if (g == 0) plan->use = total <= capacity ? 1 : 0;
+  const int64_t per_head = __shfl(incl, M - 1);
+  int64_t hs = per_head > 0 ? capacity / per_head : H;
+  hs = per_head >= cap ? 0 : (hs < H ? hs : H);
+  if (g < M) plan->off[g] = hs * (incl - bytes);
+  if (g == 0) plan->heads = (int32_t)hs;
 }
 
 // Groups by decreasing size and the prefix count of (head, tile) items.
@@ -729,7 +749,7 @@ int launch_bwd(const uint16_t* Qp, const uint16_t* Kp, const uint16_t* Vp, const
                                                                            M, N, rs, scale, dK, dV, nullptr, nullptr);
   MOGA_LAUNCH_CHECK();
   // Both dQ kernels are launched when dS may be staged; the plan (written on
-  // the device) lets exactly one of them do the work.
+  // the device) gives each head's work items to exactly one of them.
   dq_kernel<D><<<dim3((unsigned)gq), kDqWaves * kWave, 0, st>>>(Qp, Kp, Vp, dAp, lse, delta, cu, perm, sq, M, N, rs,
                                                                  scale, dQ, plan);
   MOGA_LAUNCH_CHECK();
