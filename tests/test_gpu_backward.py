@@ -159,6 +159,38 @@ def test_backward_staged(moga, N, H, D, M, d):
     assert diff.item() <= 1e-2
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_backward_staged_block_edges(moga, D):
+    """Group sizes at the 32-row block edges (odd and even block counts,
+    partial key and query blocks, the zero padding block, one-row groups):
+    the staged form against the minimum-workspace form on the same saved
+    state -- dK and dV bitwise, dQ within float32 rounding."""
+    sizes = [1, 31, 32, 33, 63, 64, 65, 255, 256, 257]
+    N, H, M = sum(sizes), 2, len(sizes)
+    print(f"[backward] staged block edges D={D} sizes={sizes}", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(91 + D)
+    Qp, Kp, Vp, dO = (torch.randn(N, H, D, generator=g, device=DEV).bfloat16() for _ in range(4))
+    cu = torch.tensor([0] + list(np.cumsum(sizes)), dtype=torch.int32, device=DEV)
+    perm = torch.arange(N, dtype=torch.int32, device=DEV)
+    gate = torch.ones(N, dtype=torch.float32, device=DEV)
+    Op, lse = moga.moga_group_attention_train(Qp, Kp, Vp, cu)
+    dOp, delta, _ = moga.moga_unpermute_backward(dO, Op, perm, gate)
+    need = moga.moga_attention_backward_staged_bytes(cu, H)
+    nb = [(n + 31) // 32 for n in sizes]
+    assert need == 4096 + H * sum(b * (b + b % 2) for b in nb) * 2048
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    a = moga.moga_group_attention_backward(Qp, Kp, Vp, dOp, lse, delta, cu, perm, 0.0, ws=ws)
+    b = moga.moga_group_attention_backward(Qp, Kp, Vp, dOp, lse, delta, cu, perm, 0.0)
+    torch.cuda.synchronize()
+    assert moga.moga_attention_backward_staged(ws) == H
+    for t in a:
+        assert torch.isfinite(t.float()).all()
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+    diff = (a[0].float() - b[0].float()).norm() / b[0].float().norm()
+    print(f"[backward] staged block edges D={D}: dQ rel_fro vs unstaged {diff.item():.2e}", flush=True)
+    assert diff.item() <= 1e-2
+
+
 def test_backward_staged_partial(moga):
     """A workspace one byte short of all heads' dS: the device plan keeps the
     first H-1 heads; the last head's dQ is the minimum-workspace result bit
