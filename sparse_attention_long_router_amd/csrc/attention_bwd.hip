@@ -8,7 +8,8 @@
 // where dA is the gated upstream gradient in permuted order and delta the
 // row sums of dA * A (both from moga_unpermute_backward).
 //
-// Two kernels, no atomics (results are bitwise repeatable):
+// Two kernels, a third for the staged form below; no atomics (results are
+// bitwise repeatable):
 //   dkdv_kernel: K and V rows of 32 keys per wave stay in registers as MFMA
 //     operands; the group's queries stream through LDS in tiles of 128 (Q,
 //     dA, lse, delta).  S = Q K^T puts one key per lane, so P and dS feed
@@ -22,9 +23,10 @@
 // dq kernel rounds it to anyway, and dq_ds_kernel computes dQ = c dS K from
 // it: five products per group and head instead of seven (S and dP are not
 // computed a second time), for sum_g n_g^2 * 2 bytes of HBM per staged head.
-// The first Hs heads that fit are staged; dq_kernel takes the others.  The dS of group g,
-// head h is stored in blocks of 32 queries x 32 keys (2 KB): block (qb, kb)
-// at off[g] + ((h * nb + qb) * nbp + kb) * 2048 bytes, nb = ceil(n_g / 32),
+// The first Hs heads that fit are staged; dq_kernel takes the others.  The
+// dS of group g, head h is stored in blocks of 32 queries x 32 keys (2 KB):
+// block (qb, kb) at off[g] + ((h * nb + qb) * nbp + kb) * 2048 bytes, with
+// nb = ceil(n_g / 32),
 // nbp = nb rounded up to even (the padding block holds zeros).  A block is
 // two 1 KB halves u = 0, 1, each 64 chunks of 16 bytes, chunk L = the 8
 // queries at positions 16u + 8(L/32) .. 16u + 8(L/32) + 7 of key L%32, so
@@ -68,7 +70,7 @@ constexpr int kDsTile = 64;    // keys per streamed LDS tile (dq_ds_kernel): two
 constexpr int kDsBlock = 2048; // bytes of one 32 x 32 dS block
 constexpr int kCpolNt = 2;     // cache policy of the dS stores and loads: non-temporal, each byte is moved once
 
-// Where the staged dS of each group starts, and whether it fits the workspace.
+// Where the staged dS of each group starts, and how many heads fit the workspace.
 struct DsPlan {
   int64_t off[kMaxGroups];  // byte offset of group g's blocks in the dS area
   int32_t heads;            // heads 0 .. heads-1 are staged: dkdv stores their dS, dq_ds_kernel forms their dQ
@@ -77,13 +79,6 @@ constexpr size_t kDsPlanOffset = 2048;  // in the workspace, after the two sched
 constexpr size_t kDsDataOffset = 4096;  // start of the dS area
 static_assert(kDsPlanOffset + offsetof(DsPlan, heads) == MOGA_BWD_STAGED_FLAG_OFFSET, "flag offset in moga.h");
 static_assert(kDsPlanOffset + sizeof(DsPlan) <= kDsDataOffset, "plan fits before the dS area");
-
-// s_waitcnt for vector memory only: at most N of this wave's loads outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
 
 __device__ __forceinline__ i32x4v byte_rsrc(const void* base, int64_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
@@ -599,9 +594,10 @@ __global__ __launch_bounds__(kDqWaves * kWave) void dq_ds_kernel(
       *reinterpret_cast<u32x4*>(Kb + (r * D + ((c ^ swz<kBoth>(r, CPR)) << 3))) = rk[sl][j];
     }
 #pragma unroll
-    for (int j = 0; j < kLoadsS; ++j)
-      *reinterpret_cast<u32x4*>(Sb + (wave * kSw + (j >> 1) * 1024 + (lane & 31) * 32 + 16 * (j & 1) + 8 * (lane >> 5))) =
-          rs[sl][j];
+    for (int j = 0; j < kLoadsS; ++j) {
+      const int o = wave * kSw + (j >> 1) * 1024 + (lane & 31) * 32 + 16 * (j & 1) + 8 * (lane >> 5);
+      *reinterpret_cast<u32x4*>(Sb + o) = rs[sl][j];
+    }
   };
   // LDS writes done, then the barrier; the empty asm statements keep the
   // compiler from moving LDS accesses across it (s_barrier itself names no
