@@ -159,16 +159,13 @@ def test_backward_staged(moga, N, H, D, M, d):
     assert diff.item() <= 1e-2
 
 
-@pytest.mark.parametrize("D", [64, 128])
-def test_backward_staged_block_edges(moga, D):
-    """Group sizes at the 32-row block edges (odd and even block counts,
-    partial key and query blocks, the zero padding block, one-row groups):
-    the staged form against the minimum-workspace form on the same saved
-    state -- dK and dV bitwise, dQ within float32 rounding."""
-    sizes = [1, 31, 32, 33, 63, 64, 65, 255, 256, 257]
-    N, H, M = sum(sizes), 2, len(sizes)
-    print(f"[backward] staged block edges D={D} sizes={sizes}", flush=True)
-    g = torch.Generator(device=DEV).manual_seed(91 + D)
+def _staged_vs_unstaged(moga, sizes, H, D, seed, label):
+    """The staged form against the minimum-workspace form on the same saved
+    state (random Q, K, V, dO in permuted order, groups of the given sizes):
+    dK and dV bitwise, dQ within float32 rounding."""
+    N, M = sum(sizes), len(sizes)
+    print(f"[backward] {label} D={D} H={H} sizes={sizes}", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(seed)
     Qp, Kp, Vp, dO = (torch.randn(N, H, D, generator=g, device=DEV).bfloat16() for _ in range(4))
     cu = torch.tensor([0] + list(np.cumsum(sizes)), dtype=torch.int32, device=DEV)
     perm = torch.arange(N, dtype=torch.int32, device=DEV)
@@ -187,8 +184,33 @@ def test_backward_staged_block_edges(moga, D):
         assert torch.isfinite(t.float()).all()
     assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
     diff = (a[0].float() - b[0].float()).norm() / b[0].float().norm()
-    print(f"[backward] staged block edges D={D}: dQ rel_fro vs unstaged {diff.item():.2e}", flush=True)
+    print(f"[backward] {label} D={D}: dQ rel_fro vs unstaged {diff.item():.2e}", flush=True)
     assert diff.item() <= 1e-2
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_backward_staged_block_edges(moga, D):
+    """Group sizes at the 32-row block edges: odd and even block counts,
+    partial key and query blocks, the zero padding block, one-row groups."""
+    _staged_vs_unstaged(moga, [1, 31, 32, 33, 63, 64, 65, 255, 256, 257], 2, D, 91 + D, "staged block edges")
+
+
+def _staged_sweep(seed, count):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        M = int(rng.integers(1, 33))
+        sizes = rng.multinomial(int(rng.integers(1, 6001)), rng.dirichlet(np.full(M, 0.7))).tolist()
+        out.append((sizes, int(rng.integers(1, 4)), int(rng.choice([64, 128]))))
+    return out
+
+
+@pytest.mark.parametrize("sizes,H,D", _staged_sweep(2026, 8))
+def test_backward_staged_sweep(moga, sizes, H, D):
+    """Seeded random group sizes (empty groups included), heads and widths."""
+    if sum(sizes) == 0:
+        sizes[0] = 1
+    _staged_vs_unstaged(moga, sizes, H, D, 97 + sum(sizes), "staged sweep")
 
 
 def test_backward_staged_partial(moga):
