@@ -279,6 +279,17 @@ def test_backward_workspace_and_argument_errors(lib):
     assert b(*args[:8], 0, *args[9:]) == ESHAPE
     assert b(*args[:11], 65, *args[12:]) == EUNSUP
     assert b(*args[:17], nbb - 1, None) == EWS
+    # the staged-dS workspace: 4 KB + H * sum_g ceil(n/32) * (that rounded up to even) * 2 KB
+    sb = lib.moga_attention_backward_staged_bytes
+    cu = (ctypes.c_int32 * 6)(0, 1, 1, 33, 100, 357)  # sizes 1, 0, 32, 67, 257 -> blocks 1, 0, 1, 3, 9
+    assert sb(cu, 5, 3) == 4096 + 3 * (1 * 2 + 0 + 1 * 2 + 3 * 4 + 9 * 10) * 2048
+    assert sb(None, 5, 3) == 0 and sb(cu, 0, 3) == 0 and sb(cu, 65, 3) == 0 and sb(cu, 5, 0) == 0
+    bad = (ctypes.c_int32 * 3)(0, 10, 5)  # a negative group size
+    assert sb(bad, 2, 1) == 0
+    huge = (ctypes.c_int32 * 2)(0, (1 << 24) + 64)  # above 2^24 tokens in one group
+    assert sb(huge, 1, 1) == 0
+    ok = (ctypes.c_int32 * 2)(0, 1 << 24)
+    assert sb(ok, 1, 1) == 4096 + (1 << 19) * (1 << 19) * 2048
     r = lib.moga_route_backward
     nr = ws(6, 100, 4, 1, 128)
     assert r(FAKE, FAKE, None, FAKE, None, 100, 128, 4, FAKE, FAKE, None, FAKE, nr, None, 0, None) == ENULL   # dgate
