@@ -67,6 +67,9 @@ constexpr int kBN = 64;                             // keys per LDS tile
 // this reads 6.0 GB from HBM per launch against 10.5 GB with runs of 8, in
 // the same time.
 constexpr int kXcdRun = 32;
+// Mean group size (tokens) below which the default forward path takes
+// 128-query items (MogaVtQRows128).
+constexpr int kShortGroup = 8192;
 // LDS of one CU (gfx950), and the bytes __syncthreads_or reserves for its reduction.
 constexpr int kCuLds = 160 * 1024;
 constexpr int kSyncOrLds = 256;
@@ -107,7 +110,10 @@ struct MogaRows {
   const int32_t* cu;
   const AttnSchedule* sched;
   int M, H;
-  __device__ __forceinline__ bool decode(int item, Work& w) const {
+  // item -> (group, head, query tile of QT queries); the schedule counts
+  // tiles of the same size
+  template <int QT>
+  __device__ __forceinline__ bool decode_tiles(int item, Work& w) const {
     const int total = sched->prefix[M];
     if (item >= total) return false;
     int i = 0;
@@ -116,14 +122,15 @@ struct MogaRows {
     const int local = item - sched->prefix[i];
     const int lo = cu[g];
     const int len = cu[g + 1] - lo;
-    const int nt = (len + kBM - 1) / kBM;
+    const int nt = (len + QT - 1) / QT;
     w.len = len;
     w.nq = len;
     w.head = local / nt;
-    w.q0 = (local - w.head * nt) * kBM;
+    w.q0 = (local - w.head * nt) * QT;
     w.row0 = lo;
     return true;
   }
+  __device__ __forceinline__ bool decode(int item, Work& w) const { return decode_tiles<kBM>(item, w); }
   __device__ __forceinline__ int64_t row(const Work& w, int i) const { return w.row0 + i; }
   __device__ __forceinline__ int64_t key(const Work& w, int i) const { return w.row0 + i; }
 };
@@ -150,6 +157,16 @@ struct MogaVtRows {
 struct MogaVtQRows : MogaVtRows {
   const int32_t* perm;
   __device__ __forceinline__ int64_t row(const Work& w, int i) const { return perm[w.row0 + i]; }
+};
+
+// MogaVtQRows in 128-query items (four waves, two workgroups per CU, as the
+// STGA windows): for short groups, where each item's fixed work (first
+// tiles, query rows, epilogue) weighs more and one item's fixed work then
+// runs beside the other's tiles.  Long groups keep 256-query items, which
+// stream every K/V tile for twice as many queries.
+struct MogaVtQRows128 : MogaVtQRows {
+  static constexpr int kQueries = 128;
+  __device__ __forceinline__ bool decode(int item, Work& w) const { return base.decode_tiles<128>(item, w); }
 };
 
 // Learned groups read in place (gather on load): permuted row j of a group is
@@ -1139,7 +1156,7 @@ __global__ __launch_bounds__((waves_for<Rows, QB>() * kWave), 2) void attn_kerne
 // One wave: groups sorted by decreasing size (ties: lower id first) and the
 // prefix count of (head, query-tile) items in that order.
 __global__ __launch_bounds__(kWave) void schedule_kernel(const int32_t* __restrict__ cu, int M, int H,
-                                                       AttnSchedule* __restrict__ sched) {
+                                                       AttnSchedule* __restrict__ sched, int qtile = kBM) {
   __shared__ int order_s[kMaxGroups];
   const int g = threadIdx.x;
   const int n = g < M ? cu[g + 1] - cu[g] : -1;
@@ -1156,7 +1173,7 @@ __global__ __launch_bounds__(kWave) void schedule_kernel(const int32_t* __restri
   if (g < M) {
     const int og = order_s[g];
     sched->order[g] = og;
-    tiles = (cu[og + 1] - cu[og] + kBM - 1) / kBM * H;
+    tiles = (cu[og + 1] - cu[og] + qtile - 1) / qtile * H;
   }
   // inclusive scan across the wave
   int incl = tiles;
@@ -1347,17 +1364,28 @@ extern "C" int moga_group_attention_unpermute_vtq(const void* Q, const void* Kp,
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
   hipStream_t st = as_stream(stream);
   auto* sched = static_cast<AttnSchedule*>(ws);
-  schedule_kernel<<<1, kWave, 0, st>>>(cu_seqlens, M, H, sched);
+  // Groups of fewer than kShortGroup tokens on average take 128-query items.
+  const bool short_groups = N < (int64_t)kShortGroup * M;
+  const int qtile = short_groups ? MogaVtQRows128::kQueries : kBM;
+  schedule_kernel<<<1, kWave, 0, st>>>(cu_seqlens, M, H, sched, qtile);
   MOGA_LAUNCH_CHECK();
-  MogaVtQRows rows;
+  MogaVtQRows128 rows;
   rows.base = MogaRows{cu_seqlens, sched, M, H};
   rows.ldv = vt_row_length(N);
   rows.perm = perm;
-  const int64_t bound = (ceil_div(N, kBM) + M) * H;
+  const int64_t bound = (ceil_div(N, qtile) + M) * H;
   const Epilogue epi{1.f, beta, nullptr, gate, nullptr, 0};
+  const MogaVtQRows& rows256 = rows;
+  if (short_groups) {
+    if (D == 128)
+      return launch_attn<128, MogaVtQRows128, kEpiGatedInPlace>(Q, Kp, Vt, O, (int64_t)H * D, scale, epi, rows, bound,
+                                                                st);
+    return launch_attn<64, MogaVtQRows128, kEpiGatedInPlace>(Q, Kp, Vt, O, (int64_t)H * D, scale, epi, rows, bound, st);
+  }
   if (D == 128)
-    return launch_attn<128, MogaVtQRows, kEpiGatedInPlace>(Q, Kp, Vt, O, (int64_t)H * D, scale, epi, rows, bound, st);
-  return launch_attn<64, MogaVtQRows, kEpiGatedInPlace>(Q, Kp, Vt, O, (int64_t)H * D, scale, epi, rows, bound, st);
+    return launch_attn<128, MogaVtQRows, kEpiGatedInPlace>(Q, Kp, Vt, O, (int64_t)H * D, scale, epi, rows256, bound,
+                                                           st);
+  return launch_attn<64, MogaVtQRows, kEpiGatedInPlace>(Q, Kp, Vt, O, (int64_t)H * D, scale, epi, rows256, bound, st);
 }
 
 extern "C" size_t moga_stga_shot_workspace_bytes(int32_t T, int32_t n_shots, int32_t win_t) {

@@ -105,6 +105,8 @@ def test_tiny_workload(moga):
     (5, 2, 64, 3),          # fewer tokens than a tile
     (4097, 3, 128, 16),
     (700, 64, 128, 4),      # H * D = 8192, the widest supported token row
+    (16000, 1, 64, 2),      # mean group 8,000 tokens: the default path's 128-query items
+    (17000, 1, 128, 2),     # mean group 8,500 tokens: its 256-query items
 ])
 def test_shapes(moga, N, H, D, M):
     _full_check(moga, _inputs("wan13b_21f", N=N, H=H, D=D, M=M, d_model=256), label=f"shape{N}")
